@@ -1,0 +1,331 @@
+"""CPU oracle of the AuT audio-encoder forward pass (test infrastructure).
+
+Plain, slow, float64 numpy.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may use this module; the product path never does.
+It shares no code with the HIP library and imports nothing from it.
+
+What it follows (the pages are cited by title and section):
+
+* "mstar.model.components.aut_encoder" (m-star API page), module summary:
+  1 s chunks of 2*n_window frames; three stride-2 Conv2d layers (100 frames ->
+  13 tokens); linear conv_out; the same 13 sinusoidal positions per chunk;
+  valid tokens packed into one [total_tokens, d_model] sequence; attention
+  within windows of n_window_infer frames (8 s -> 104 tokens), block-diagonal,
+  bidirectional, no cache; final LayerNorm and a two-layer GELU projector.
+  ``frontend``: the last piece is zero-padded to a full chunk, convolved and
+  trimmed back to its valid tokens.  ``tokens_for_frames``: 13 per full chunk
+  plus three stride-2 convolutions' worth of the remainder.
+  ``window_lengths``: full windows, then the remainder.  SDPA per window from
+  cu_seqlens is the attention's definition.  q/k/v are fused into qkv_proj.
+* "1A - AuT Audio Encoder" (openarchlab course), section 3: Conv2d(k=3, s=2,
+  p=1) maps L to floor((L+1)/2); 128 bins -> 16; flatten C_conv x 16 and a
+  linear conv_out to d_model; non-causal attention inside cu_seqlens segments;
+  projector Linear(d -> d) + GELU + Linear(d -> 2048).
+* "Audio Encoder Component" (cubic.dev wiki), Transformer Encoder Layers:
+  LayerNorm with bias (not RMSNorm); sinusoidal positions computed, not loaded.
+
+Readings where the pages are silent (listed with reasons in the repository's
+design notes): Whisper-style [sin | cos] table with increment
+ln(10000)/(d/2 - 1); chunk-local positions 0..k-1; exact (erf) GELU after each
+conv, fc1 and proj1; LayerNorm eps 1e-5 with population variance; pre-LN
+residual order; attention scale 1/sqrt(head_dim); flatten index c*16 + f;
+conv_out without bias unless one is given; H axis = mel bin, W axis = time;
+padding beyond a request's length is treated as zero whatever it holds.
+
+Parity pins: see tests/test_oracle_pins.py.  Every function below is pinned by
+at least one test against a library routine, a closed form, a value printed on
+the pages, or an exact invariant.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf as _erf
+
+# ---------------------------------------------------------------------------
+# plan (host arithmetic only)
+# ---------------------------------------------------------------------------
+
+
+def conv_out_len(n: int) -> int:
+    """Output length of Conv2d(kernel 3, stride 2, padding 1) along one axis:
+    floor((n + 1) / 2) -- openarchlab "1A", section 3 formula."""
+    return (n + 1) // 2
+
+
+def chunk_frames(cfg: dict) -> int:
+    """Frames per chunk: 2 * n_window (m-star API page, module summary)."""
+    return 2 * cfg["n_window"]
+
+
+def tokens_for_frames(num_frames: int, cfg: dict) -> int:
+    """m-star ``tokens_for_frames``: per full chunk the three-conv output
+    length of a full chunk; for the remainder, three halvings of its length."""
+    cf = chunk_frames(cfg)
+    per_chunk = conv_out_len(conv_out_len(conv_out_len(cf)))
+    full, rem = divmod(int(num_frames), cf)
+    return full * per_chunk + conv_out_len(conv_out_len(conv_out_len(rem)))
+
+
+def window_tokens(cfg: dict) -> int:
+    """Tokens per attention window: n_window_infer frames is a whole number of
+    chunks (8 s = 8 chunks -> 104 tokens on the m-star page)."""
+    cf = chunk_frames(cfg)
+    if cfg["n_window_infer"] % cf:
+        raise ValueError("n_window_infer must be a multiple of 2*n_window")
+    per_chunk = tokens_for_frames(cf, cfg)
+    return per_chunk * (cfg["n_window_infer"] // cf)
+
+
+def window_lengths(num_tokens: int, cfg: dict) -> list[int]:
+    """m-star ``window_lengths``: full windows, then the remainder (if any)."""
+    wt = window_tokens(cfg)
+    full, rem = divmod(int(num_tokens), wt)
+    return [wt] * full + ([rem] if rem else [])
+
+
+def plan(feature_lens, cfg: dict) -> dict:
+    """m-star ``layout``: tokens per request and cu_seqlens for a batch, plus
+    the chunk table the frontend walks.
+
+    Packed row order: request, then chunk, then token within the chunk.
+    Windows never span two requests; an empty request adds nothing.
+    """
+    cf = chunk_frames(cfg)
+    chunks = []            # (request, first frame, valid frames, valid tokens, first row)
+    tokens_per_request = []
+    cu = [0]
+    row = 0
+    for b, L in enumerate(feature_lens):
+        L = int(L)
+        if L < 0:
+            raise ValueError("negative feature length")
+        n_chunks = -(-L // cf)
+        t_req = 0
+        for c in range(n_chunks):
+            vf = min(cf, L - c * cf)
+            vt = tokens_for_frames(vf, cfg)
+            chunks.append((b, c * cf, vf, vt, row))
+            row += vt
+            t_req += vt
+        assert t_req == tokens_for_frames(L, cfg)
+        tokens_per_request.append(t_req)
+        for wl in window_lengths(t_req, cfg):
+            cu.append(cu[-1] + wl)
+    return dict(
+        chunks=chunks,
+        tokens_per_request=tokens_per_request,
+        cu_seqlens=cu,
+        total_tokens=row,
+        window_lengths=[cu[i + 1] - cu[i] for i in range(len(cu) - 1)],
+    )
+
+
+# ---------------------------------------------------------------------------
+# elementary operations
+# ---------------------------------------------------------------------------
+
+
+def gelu(x):
+    """Exact GELU, x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)) ('gelu' in
+    AuTEncoderConfig.activation_function)."""
+    return 0.5 * x * (1.0 + _erf(x / math.sqrt(2.0)))
+
+
+def sinusoid_table(length: int, channels: int) -> np.ndarray:
+    """Fixed sinusoidal position table [length, channels] (wiki "Positional
+    Embeddings": computed, not loaded).  Whisper-style: row j, column i < D is
+    sin(j * tau_i), column D + i is cos(j * tau_i), tau_i = 10000^(-i/(D-1)),
+    D = channels / 2."""
+    if channels % 2:
+        raise ValueError("channels must be even")
+    D = channels // 2
+    inc = math.log(10000.0) / (D - 1)
+    tau = np.exp(-inc * np.arange(D, dtype=np.float64))
+    t = np.arange(length, dtype=np.float64)[:, None] * tau[None, :]
+    return np.concatenate([np.sin(t), np.cos(t)], axis=1)
+
+
+def conv2d_k3s2p1(x: np.ndarray, w: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """2-D cross-correlation, kernel 3x3, stride 2, zero padding 1 (openarchlab
+    "1A", glossary and section 3), plus bias.
+
+    x [Cin, H, W], w [Cout, Cin, 3, 3], b [Cout] -> [Cout, floor((H+1)/2),
+    floor((W+1)/2)].  out[o, y, t] = b[o] + sum_{i, kh, kw} w[o, i, kh, kw] *
+    xpad[i, 2y + kh, 2t + kw], written as a sum over the nine taps of a
+    channel contraction.
+    """
+    cin, H, W = x.shape
+    Ho, Wo = conv_out_len(H), conv_out_len(W)
+    xp = np.zeros((cin, H + 2, W + 2), dtype=np.float64)
+    xp[:, 1:H + 1, 1:W + 1] = x
+    out = np.zeros((w.shape[0], Ho, Wo), dtype=np.float64)
+    for kh in range(3):
+        for kw in range(3):
+            patch = xp[:, kh:kh + 2 * Ho:2, kw:kw + 2 * Wo:2]        # [Cin, Ho, Wo]
+            out += np.tensordot(w[:, :, kh, kw].astype(np.float64), patch, axes=(1, 0))
+    out += np.asarray(b, dtype=np.float64)[:, None, None]
+    return out
+
+
+def layer_norm(x: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float = 1e-5):
+    """LayerNorm with bias over the last axis: population variance, eps inside
+    the square root (wiki: "LayerNorm with bias")."""
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * g + b
+
+
+def linear(x: np.ndarray, w: np.ndarray, b=None) -> np.ndarray:
+    """y = x W^T (+ b), W in [out, in] layout."""
+    y = x @ np.asarray(w, dtype=np.float64).T
+    if b is not None:
+        y = y + np.asarray(b, dtype=np.float64)
+    return y
+
+
+def softmax(s: np.ndarray, axis: int = -1) -> np.ndarray:
+    m = s.max(axis=axis, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=axis, keepdims=True)
+
+
+def window_attention(q, k, v, cu_seqlens, num_heads: int) -> np.ndarray:
+    """SDPA per window (m-star AuTAttention, unbound case): for each segment
+    [s, e) of cu_seqlens and each head, softmax(Q K^T / sqrt(hd)) V with no
+    mask inside the segment and nothing across segments (bidirectional,
+    is_causal = False)."""
+    T, d = q.shape
+    hd = d // num_heads
+    out = np.zeros((T, d), dtype=np.float64)
+    scale = 1.0 / math.sqrt(hd)
+    for w in range(len(cu_seqlens) - 1):
+        s, e = int(cu_seqlens[w]), int(cu_seqlens[w + 1])
+        for h in range(num_heads):
+            cols = slice(h * hd, (h + 1) * hd)
+            qh, kh, vh = q[s:e, cols], k[s:e, cols], v[s:e, cols]
+            p = softmax((qh @ kh.T) * scale, axis=-1)
+            out[s:e, cols] = p @ vh
+    return out
+
+
+# ---------------------------------------------------------------------------
+# the encoder
+# ---------------------------------------------------------------------------
+
+
+def chunk_image(features: np.ndarray, b: int, frame0: int, valid: int, cfg: dict):
+    """One chunk as a 1-channel image [1, mel, chunk_frames]: the valid frames
+    of request b, then zeros (the m-star ``frontend`` zero-pads the last piece
+    to a full chunk).  Buffer contents past the length are never read."""
+    cf = chunk_frames(cfg)
+    img = np.zeros((1, cfg["num_mel_bins"], cf), dtype=np.float64)
+    img[0, :, :valid] = features[b, :, frame0:frame0 + valid]
+    return img
+
+
+def conv_stem(img: np.ndarray, P: dict) -> np.ndarray:
+    """Three Conv2d(k3, s2, p1) layers, each followed by GELU:
+    [1, 128, 100] -> [C, 16, 13]."""
+    a = gelu(conv2d_k3s2p1(img, P["conv1_w"], P["conv1_b"]))
+    a = gelu(conv2d_k3s2p1(a, P["conv2_w"], P["conv2_b"]))
+    a = gelu(conv2d_k3s2p1(a, P["conv3_w"], P["conv3_b"]))
+    return a
+
+
+def flatten_tokens(a3: np.ndarray, vt: int) -> np.ndarray:
+    """The first vt time columns of the stem output [C, 16, 13] as token rows
+    [vt, C * 16], flattened channel-major: u_j[c * 16 + f] = a3[c, f, j]
+    (openarchlab "1A", section 3: flatten C_conv x 16)."""
+    C, Fq, _ = a3.shape
+    return a3[:, :, :vt].transpose(2, 0, 1).reshape(vt, C * Fq)
+
+
+def frontend(features, feature_lens, P: dict, cfg: dict, chunk_ids=None):
+    """m-star ``frontend``: chunk, pad, convolve, conv_out, add positions,
+    keep the valid tokens.  Returns ([rows, d_model], the plan); ``chunk_ids``
+    restricts the work to some chunks (rows returned in chunk order)."""
+    pl = plan(feature_lens, cfg)
+    d = cfg["d_model"]
+    pe = sinusoid_table(cfg["max_source_positions"], d)
+    ids = range(len(pl["chunks"])) if chunk_ids is None else chunk_ids
+    rows = []
+    for ci in ids:
+        b, f0, vf, vt, _ = pl["chunks"][ci]
+        a3 = conv_stem(chunk_image(features, b, f0, vf, cfg), P)       # [C, 16, 13]
+        u = flatten_tokens(a3, vt)
+        e = linear(u, P["conv_out_w"], P.get("conv_out_b"))
+        e = e + pe[:vt]
+        rows.append(e)
+    if rows:
+        return np.concatenate(rows, axis=0), pl
+    return np.zeros((0, d)), pl
+
+
+def encoder_layer(x: np.ndarray, cu_seqlens, P: dict, i: int, cfg: dict):
+    """One pre-LN layer: x += Attn(LN1 x); x += FFN(LN2 x) with
+    FFN(y) = fc2(GELU(fc1 y)).  qkv rows are [q; k; v]."""
+    p = f"layers.{i}."
+    d = cfg["d_model"]
+    h = layer_norm(x, P[p + "ln1_g"], P[p + "ln1_b"])
+    qkv = linear(h, P[p + "qkv_w"], P.get(p + "qkv_b"))
+    q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    o = window_attention(q, k, v, cu_seqlens, cfg["encoder_attention_heads"])
+    x = x + linear(o, P[p + "o_w"], P.get(p + "o_b"))
+    h = layer_norm(x, P[p + "ln2_g"], P[p + "ln2_b"])
+    f = gelu(linear(h, P[p + "fc1_w"], P.get(p + "fc1_b")))
+    x = x + linear(f, P[p + "fc2_w"], P.get(p + "fc2_b"))
+    return x
+
+
+def encode(hidden: np.ndarray, cu_seqlens, P: dict, cfg: dict) -> np.ndarray:
+    """m-star ``encode``: the layer stack and projector over a packed
+    sequence, (total_tokens, d_model) -> (total_tokens, output_dim)."""
+    x = np.asarray(hidden, dtype=np.float64)
+    for i in range(cfg["encoder_layers"]):
+        x = encoder_layer(x, cu_seqlens, P, i, cfg)
+    y = layer_norm(x, P["ln_post_g"], P["ln_post_b"])
+    y = gelu(linear(y, P["proj1_w"], P.get("proj1_b")))
+    return linear(y, P["proj2_w"], P.get("proj2_b"))
+
+
+def forward(features, feature_lens, P: dict, cfg: dict):
+    """m-star ``forward``: (output [total_tokens, output_dim], layout)."""
+    hidden, pl = frontend(features, feature_lens, P, cfg)
+    return encode(hidden, pl["cu_seqlens"], P, cfg), pl
+
+
+def window_chunks(pl: dict, cfg: dict) -> list[list[int]]:
+    """Chunk ids of each window: a window is a whole number of chunks of one
+    request, because window_tokens is a multiple of the tokens per chunk."""
+    cu = pl["cu_seqlens"]
+    out = []
+    ci = 0
+    for w in range(len(cu) - 1):
+        s, e = cu[w], cu[w + 1]
+        ids = []
+        while ci < len(pl["chunks"]) and pl["chunks"][ci][4] < e:
+            assert pl["chunks"][ci][4] >= s
+            ids.append(ci)
+            ci += 1
+        out.append(ids)
+    return out
+
+
+def forward_windows(features, feature_lens, P: dict, cfg: dict, windows):
+    """Exact output rows of selected windows only.
+
+    Windows are independent end to end (block-diagonal attention, per-row
+    everything else), so a window's rows depend on its own chunks alone.
+    Returns {window id: (first row, [rows, output_dim])}.
+    """
+    pl = plan(feature_lens, cfg)
+    wch = window_chunks(pl, cfg)
+    res = {}
+    for w in windows:
+        ids = wch[w]
+        hidden, _ = frontend(features, feature_lens, P, cfg, chunk_ids=ids)
+        n = hidden.shape[0]
+        res[w] = (pl["cu_seqlens"][w], encode(hidden, [0, n], P, cfg))
+    return res

@@ -1,0 +1,362 @@
+"""Pins of the oracle's arithmetic against things other than itself.
+
+Each ``check_*`` function compares one oracle function with a library routine
+(torch float64 on the CPU), a closed form, or an exact invariant, and returns
+the largest deviation.  ``test_planted_mistakes`` then plants plausible
+mistakes in the oracle (a transposed kernel, a dropped bias, a causal mask, a
+wrong variance, a swapped flatten order, ...) and requires the corresponding
+check to catch each one: the pins are shown to be able to fail.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as Fn
+
+import oracle
+import oracle.aut_oracle as ao
+import synth_inputs as si
+
+RNG = np.random.default_rng(1234)
+
+
+def small_cfg(**kw):
+    cfg = dict(num_mel_bins=128, n_window=50, n_window_infer=800, conv_chunksize=500,
+               output_dim=96, max_source_positions=1500, d_model=128, encoder_layers=2,
+               encoder_attention_heads=2, encoder_ffn_dim=256, downsample_hidden_size=8,
+               conv_out_bias=False, dtype="fp32")
+    cfg.update(kw)
+    return cfg
+
+
+# ---------------------------------------------------------------------------
+# checks: each returns a max deviation
+# ---------------------------------------------------------------------------
+
+
+def check_gelu():
+    x = np.linspace(-8, 8, 4001)
+    ref = Fn.gelu(torch.from_numpy(x), approximate="none").numpy()
+    e1 = np.abs(ao.gelu(x) - ref).max()
+    # exact identities: gelu(x) - gelu(-x) = x, gelu(0) = 0
+    e2 = np.abs(ao.gelu(x) - ao.gelu(-x) - x).max()
+    return max(e1, e2, abs(ao.gelu(np.array(0.0))))
+
+
+def check_pe():
+    d = 1280
+    D = d // 2
+    pe = ao.sinusoid_table(1500, d)
+    j = np.arange(1500)
+    errs = [
+        np.abs(pe[0, :D]).max(),
+        np.abs(pe[0, D:] - 1).max(),
+        np.abs(pe[:, 0] - np.sin(j)).max(),
+        np.abs(pe[:, D] - np.cos(j)).max(),
+        np.abs(pe[:, D - 1] - np.sin(j * 1e-4)).max(),
+        np.abs(pe[:, 2 * D - 1] - np.cos(j * 1e-4)).max(),
+        np.abs(pe[:, :D] ** 2 + pe[:, D:] ** 2 - 1).max(),
+    ]
+    # frequencies form a geometric progression from 1 down to 1e-4
+    freq = np.arcsin(pe[1, :D])  # row 1 holds sin(tau_i), tau_i <= 1 < pi/2
+    ratio = freq[1:] / freq[:-1]
+    errs.append(np.abs(ratio - 1e-4 ** (1.0 / (D - 1))).max())
+    return max(errs)
+
+
+def check_conv():
+    errs = []
+    for cin, cout, H, W in [(1, 5, 128, 100), (3, 4, 9, 7), (2, 2, 64, 50), (4, 3, 32, 25)]:
+        x = RNG.standard_normal((cin, H, W))
+        w = RNG.standard_normal((cout, cin, 3, 3))
+        b = RNG.standard_normal(cout)
+        ref = Fn.conv2d(torch.from_numpy(x)[None], torch.from_numpy(w), torch.from_numpy(b),
+                        stride=2, padding=1)[0].numpy()
+        got = ao.conv2d_k3s2p1(x, w, b)
+        if got.shape != ref.shape:
+            return float("inf")
+        errs.append(np.abs(got - ref).max())
+    # special case: centre-tap identity kernel = stride-2 subsampling
+    x = RNG.standard_normal((3, 11, 10))
+    w = np.zeros((3, 3, 3, 3))
+    for i in range(3):
+        w[i, i, 1, 1] = 1.0
+    errs.append(np.abs(ao.conv2d_k3s2p1(x, w, np.zeros(3)) - x[:, ::2, ::2]).max())
+    return max(errs)
+
+
+def check_ln():
+    x = RNG.standard_normal((17, 96)) * 3 + 1.5
+    g = RNG.standard_normal(96)
+    b = RNG.standard_normal(96)
+    ref = Fn.layer_norm(torch.from_numpy(x), (96,), torch.from_numpy(g), torch.from_numpy(b),
+                        eps=1e-5).numpy()
+    e1 = np.abs(ao.layer_norm(x, g, b) - ref).max()
+    # a constant row normalises to the shift exactly
+    c = np.full((2, 96), 3.25)
+    e2 = np.abs(ao.layer_norm(c, g, b) - b).max()
+    return max(e1, e2)
+
+
+def sdpa_windows(q, k, v, cu, H):
+    out = torch.zeros(q.shape, dtype=torch.float64)
+    hd = q.shape[1] // H
+    for w in range(len(cu) - 1):
+        s, e = cu[w], cu[w + 1]
+
+        def heads(t):
+            return torch.from_numpy(t[s:e]).reshape(e - s, H, hd).transpose(0, 1)[None]
+        o = Fn.scaled_dot_product_attention(heads(q), heads(k), heads(v), is_causal=False)
+        out[s:e] = o[0].transpose(0, 1).reshape(e - s, H * hd)
+    return out.numpy()
+
+
+def check_attn():
+    T, H, hd = 230, 3, 64
+    q, k, v = (RNG.standard_normal((T, H * hd)) for _ in range(3))
+    cu = [0, 104, 105, 200, 230]
+    e1 = np.abs(ao.window_attention(q, k, v, cu, H) - sdpa_windows(q, k, v, cu, H)).max()
+    # one window over everything = dense attention
+    e2 = np.abs(ao.window_attention(q, k, v, [0, T], H) - sdpa_windows(q, k, v, [0, T], H)).max()
+    # a length-1 window returns v; equal keys return the mean of v
+    e3 = np.abs(ao.window_attention(q, k, v, cu, H)[104] - v[104]).max()
+    keq = np.tile(k[:1], (T, 1))
+    o = ao.window_attention(q, keq, v, [0, 50, T], H)
+    e4 = max(np.abs(o[:50] - v[:50].mean(0)).max(), np.abs(o[50:] - v[50:].mean(0)).max())
+    return max(e1, e2, e3, e4)
+
+
+def torch_forward(features, lens, P, cfg):
+    """Independent float64 composition of torch library routines: chunks are
+    cut with reshape and convolved as a batch, tokens flattened with
+    permute/reshape, attention by scaled_dot_product_attention per window."""
+    t = {k: torch.from_numpy(np.asarray(v, dtype=np.float64)) for k, v in P.items()}
+    d, H = cfg["d_model"], cfg["encoder_attention_heads"]
+    D = d // 2
+    inv = torch.exp(-math.log(10000.0) / (D - 1) * torch.arange(D, dtype=torch.float64))
+    pos = torch.arange(13, dtype=torch.float64)[:, None] * inv[None]
+    pe = torch.cat([pos.sin(), pos.cos()], 1)
+    rows, wl = [], []
+    for b, L in enumerate(lens):
+        L = int(L)
+        if L == 0:
+            continue
+        n = -(-L // 100)
+        x = torch.zeros(128, n * 100, dtype=torch.float64)
+        x[:, :L] = torch.from_numpy(features[b, :, :L].astype(np.float64))
+        x = x.reshape(128, n, 100).permute(1, 0, 2)[:, None]          # [n, 1, 128, 100]
+        for i in (1, 2, 3):
+            x = Fn.gelu(Fn.conv2d(x, t[f"conv{i}_w"], t[f"conv{i}_b"], stride=2, padding=1))
+        n_, C, Fq, Tq = x.shape
+        u = x.permute(0, 3, 1, 2).reshape(n, Tq, C * Fq)              # [n, 13, C*16]
+        e = Fn.linear(u, t["conv_out_w"], t.get("conv_out_b")) + pe
+        ntok = 13 * (L // 100) + -(-(L % 100) // 8)
+        rows.append(e.reshape(n * 13, d)[:ntok] if L % 100 == 0 else
+                    torch.cat([e[:-1].reshape(-1, d), e[-1, :ntok - 13 * (n - 1)]]))
+        wl += [104] * (ntok // 104) + ([ntok % 104] if ntok % 104 else [])
+    x = torch.cat(rows)
+    cu = np.cumsum([0] + wl)
+    for i in range(cfg["encoder_layers"]):
+        p = f"layers.{i}."
+        h = Fn.layer_norm(x, (d,), t[p + "ln1_g"], t[p + "ln1_b"], eps=1e-5)
+        qkv = Fn.linear(h, t[p + "qkv_w"], t[p + "qkv_b"])
+        q, k, v = qkv.split(d, dim=1)
+        o = torch.from_numpy(sdpa_windows(q.numpy(), k.numpy(), v.numpy(), cu, H))
+        x = x + Fn.linear(o, t[p + "o_w"], t[p + "o_b"])
+        h = Fn.layer_norm(x, (d,), t[p + "ln2_g"], t[p + "ln2_b"], eps=1e-5)
+        x = x + Fn.linear(Fn.gelu(Fn.linear(h, t[p + "fc1_w"], t[p + "fc1_b"])), t[p + "fc2_w"], t[p + "fc2_b"])
+    y = Fn.layer_norm(x, (d,), t["ln_post_g"], t["ln_post_b"], eps=1e-5)
+    y = Fn.linear(Fn.gelu(Fn.linear(y, t["proj1_w"], t["proj1_b"])), t["proj2_w"], t["proj2_b"])
+    return y.numpy()
+
+
+COMP = {}
+
+
+def composition_case(bias=False):
+    key = bias
+    if key not in COMP:
+        cfg = small_cfg(conv_out_bias=bias)
+        lens = np.array([250, 0, 800, 37, 1010])
+        feats = si.mel_features(lens, seed=7)
+        P = si.params(cfg, seed=7, std=0.1)
+        COMP[key] = (cfg, lens, feats, P, torch_forward(feats, lens, P, cfg))
+    return COMP[key]
+
+
+def check_composition(bias=False):
+    cfg, lens, feats, P, ref = composition_case(bias)
+    got, _ = ao.forward(feats, lens, P, cfg)
+    if got.shape != ref.shape:
+        return float("inf")
+    return np.abs(got - ref).max() / np.abs(ref).max()
+
+
+# ---------------------------------------------------------------------------
+# tests
+# ---------------------------------------------------------------------------
+
+
+def test_gelu():
+    assert check_gelu() < 1e-14
+
+
+def test_sinusoid_closed_form():
+    assert check_pe() < 1e-9
+
+
+def test_conv_vs_torch():
+    assert check_conv() < 1e-12
+
+
+def test_layer_norm_vs_torch():
+    assert check_ln() < 1e-12
+
+
+def test_window_attention_vs_sdpa():
+    assert check_attn() < 1e-12
+
+
+@pytest.mark.parametrize("bias", [False, True])
+def test_whole_path_vs_torch_composition(bias):
+    assert check_composition(bias) < 1e-12
+
+
+def test_partial_chunk_is_padded_to_full_chunk():
+    """m-star ``frontend``: the last piece is zero-padded to a full chunk,
+    convolved, then trimmed.  Convolving only the 37 valid frames gives a
+    different last token (GELU(bias) != 0 in the padded region)."""
+    cfg = small_cfg(encoder_layers=0)
+    lens = np.array([137])
+    feats = si.mel_features(lens, seed=3)
+    P = si.params(cfg, seed=3, std=0.1)
+    hid, pl = ao.frontend(feats, lens, P, cfg)
+    assert hid.shape[0] == 13 + 5
+    img = np.zeros((1, 128, 100))
+    img[0, :, :37] = feats[0, :, 100:137]
+    a = ao.conv_stem(img, P)
+    want = ao.flatten_tokens(a, 5) @ P["conv_out_w"].T.astype(np.float64) + ao.sinusoid_table(13, 128)[:5]
+    assert np.abs(hid[13:] - want).max() < 1e-12
+    short = ao.conv_stem(img[:, :, :37], P)
+    alt = ao.flatten_tokens(short, 5) @ P["conv_out_w"].T.astype(np.float64) + ao.sinusoid_table(13, 128)[:5]
+    assert np.abs(alt[:4] - want[:4]).max() < 1e-12      # early tokens agree
+    assert np.abs(alt[4] - want[4]).max() > 1e-3         # the last one does not
+
+
+def test_padding_contents_ignored():
+    cfg = small_cfg(encoder_layers=1)
+    lens = np.array([137, 301])
+    a = si.mel_features(lens, seed=5, pad_value=np.nan)
+    b = si.mel_features(lens, seed=5, pad_value=0.0)
+    c = si.mel_features(lens, seed=5, pad_value=1e30, t_max=400)
+    P = si.params(cfg, seed=5)
+    ya, _ = ao.forward(a, lens, P, cfg)
+    yb, _ = ao.forward(b, lens, P, cfg)
+    yc, _ = ao.forward(c, lens, P, cfg)
+    assert np.isfinite(ya).all()
+    assert np.array_equal(ya, yb) and np.array_equal(ya, yc)
+
+
+def test_window_isolation_bitwise():
+    """openarchlab "1A", section 4: perturbing one window's spectrogram leaves
+    every other window's output unchanged (deviation 0.00e+00)."""
+    cfg = small_cfg()
+    lens = np.array([1737, 300])
+    feats = si.mel_features(lens, seed=11)
+    P = si.params(cfg, seed=11, std=0.05)
+    y0, pl = ao.forward(feats, lens, P, cfg)
+    cu = pl["cu_seqlens"]
+    f2 = feats.copy()
+    f2[0, :, 800:1600] += 0.5            # window 1 of request 0 = frames 800..1599
+    y1, _ = ao.forward(f2, lens, P, cfg)
+    changed = [w for w in range(len(cu) - 1) if not np.array_equal(y0[cu[w]:cu[w + 1]], y1[cu[w]:cu[w + 1]])]
+    assert changed == [1]
+
+
+def test_request_permutation():
+    cfg = small_cfg(encoder_layers=1)
+    lens = np.array([250, 800, 37])
+    feats = si.mel_features(lens, seed=2)
+    P = si.params(cfg, seed=2)
+    y, pl = ao.forward(feats, lens, P, cfg)
+    perm = [2, 0, 1]
+    y2, pl2 = ao.forward(feats[perm], lens[perm], P, cfg)
+    off = np.cumsum([0] + pl["tokens_per_request"])
+    rows = np.concatenate([np.arange(off[b], off[b + 1]) for b in perm])
+    assert np.array_equal(y[rows], y2)
+
+
+def test_forward_windows_exact():
+    cfg = small_cfg()
+    lens = np.array([1737, 300, 0, 905])
+    feats = si.mel_features(lens, seed=4)
+    P = si.params(cfg, seed=4, std=0.05)
+    y, pl = ao.forward(feats, lens, P, cfg)
+    nw = len(pl["cu_seqlens"]) - 1
+    part = ao.forward_windows(feats, lens, P, cfg, range(nw))
+    for w, (r0, yw) in part.items():
+        np.testing.assert_array_equal(yw, y[r0:r0 + yw.shape[0]])
+
+
+# planted mistakes: each must make its pin fail
+
+
+MUTATIONS = {
+    "conv kernel transposed": ("conv2d_k3s2p1", lambda orig: (lambda x, w, b: orig(x, np.swapaxes(w, 2, 3), b)), check_conv),
+    "conv bias dropped": ("conv2d_k3s2p1", lambda orig: (lambda x, w, b: orig(x, w, np.zeros_like(b))), check_conv),
+    "ln unbiased variance": ("layer_norm", lambda orig: (lambda x, g, b, eps=1e-5: (x - x.mean(-1, keepdims=True)) / np.sqrt(x.var(-1, ddof=1, keepdims=True) + eps) * g + b), check_ln),
+    "ln gain/shift swapped": ("layer_norm", lambda orig: (lambda x, g, b, eps=1e-5: orig(x, b, g, eps)), check_ln),
+    "attention scale 1/hd": ("window_attention", lambda orig: (lambda q, k, v, cu, H: orig(q * (1.0 / 8.0), k, v, cu, H)), check_attn),
+    "attention causal": ("window_attention", lambda orig: _causal_attn, check_attn),
+    "attention across windows": ("window_attention", lambda orig: (lambda q, k, v, cu, H: orig(q, k, v, [cu[0], cu[-1]], H)), check_attn),
+    "pe sin/cos swapped": ("sinusoid_table", lambda orig: (lambda n, c: np.roll(orig(n, c), c // 2, axis=1)), check_pe),
+    "pe increment ln/D": ("sinusoid_table", lambda orig: _pe_wrong_inc, check_pe),
+    "gelu tanh approx": ("gelu", lambda orig: (lambda x: 0.5 * x * (1 + np.tanh(math.sqrt(2 / math.pi) * (x + 0.044715 * x ** 3)))), check_gelu),
+    "flatten f-major": ("flatten_tokens", lambda orig: (lambda a3, vt: a3[:, :, :vt].transpose(2, 1, 0).reshape(vt, -1)), check_composition),
+    "linear bias dropped": ("linear", lambda orig: (lambda x, w, b=None: orig(x, w, None)), check_composition),
+    "post-LN layer order": ("encoder_layer", lambda orig: _post_ln_layer, check_composition),
+    "qkv split k/v swapped": ("window_attention", lambda orig: (lambda q, k, v, cu, H: orig(q, v, k, cu, H)), check_composition),
+    "positions not chunk-local": ("sinusoid_table", lambda orig: (lambda n, c: orig(n + 1, c)[1:]), check_composition),
+}
+
+
+def _causal_attn(q, k, v, cu, H):
+    T, d = q.shape
+    hd = d // H
+    out = np.zeros((T, d))
+    for w in range(len(cu) - 1):
+        s, e = cu[w], cu[w + 1]
+        for h in range(H):
+            c = slice(h * hd, (h + 1) * hd)
+            sc = q[s:e, c] @ k[s:e, c].T / math.sqrt(hd)
+            sc = sc + np.triu(np.full((e - s, e - s), -np.inf), 1)
+            out[s:e, c] = ao.softmax(sc) @ v[s:e, c]
+    return out
+
+
+def _pe_wrong_inc(n, c):
+    D = c // 2
+    tau = np.exp(-math.log(10000.0) / D * np.arange(D))
+    t = np.arange(n)[:, None] * tau[None]
+    return np.concatenate([np.sin(t), np.cos(t)], 1)
+
+
+def _post_ln_layer(x, cu, P, i, cfg):
+    p = f"layers.{i}."
+    d = cfg["d_model"]
+    qkv = ao.linear(x, P[p + "qkv_w"], P[p + "qkv_b"])
+    o = ao.window_attention(qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:], cu, cfg["encoder_attention_heads"])
+    x = ao.layer_norm(x + ao.linear(o, P[p + "o_w"], P[p + "o_b"]), P[p + "ln1_g"], P[p + "ln1_b"])
+    f = ao.gelu(ao.linear(x, P[p + "fc1_w"], P[p + "fc1_b"]))
+    return ao.layer_norm(x + ao.linear(f, P[p + "fc2_w"], P[p + "fc2_b"]), P[p + "ln2_g"], P[p + "ln2_b"])
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistakes(name, monkeypatch):
+    attr, make, check = MUTATIONS[name]
+    orig = getattr(ao, attr)
+    composition_case(False)  # reference computed before patching
+    monkeypatch.setattr(ao, attr, make(orig))
+    err = check()
+    assert err > 1e-6, f"pin did not catch: {name} (err={err})"
