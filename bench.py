@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Throughput of the AuT encoder forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wide]
+
+A step is one whole forward (plan, plan upload, conv stem, conv_out +
+positions + pack, every encoder layer, final LayerNorm and projector) over the
+same synthetic batch, with features and parameters already resident in HBM.
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth_inputs as si  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix/vector peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+METRIC = "encoder tokens/s and audio-sec/s on 1 MI355X; % of bf16 MFMA peak"
+
+DESCR = {
+    "tiny": "1 request x 8 s, 1 layer, d_model 1280, 20 heads, FFN 5120, conv 128 ch, fp32",
+    "rag": "4 requests x (3, 8, 17.37, 30) s, 18 layers, d_model 1024, 16 heads, FFN 4096, conv 128 ch",
+    "wide": "64 requests x U[5, 30] s (seeded), 24 layers, d_model 1280, 20 heads x 64, FFN 5120, "
+            "conv 480 ch, conv_out 7680->1280, projector 1280->1280->2048",
+    "long": "1 request x 1200 s, 24 layers, d_model 1280, 20 heads, FFN 5120, conv 480 ch",
+    "conc": "512 requests x lognormal(median 7 s, sigma 0.6) in [0.5, 35] s, 24 layers, d_model 1280",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(name, cfg_d, lens, feats, P, n_windows):
+    """The float64 oracle on a bounded sample of the same workload's windows."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    pl = oracle.plan(lens, cfg_d)
+    nw = len(pl["window_lengths"])
+    rng = np.random.default_rng(1000 + si.workload_seed(name))
+    wins = sorted({0} | set(int(w) for w in rng.choice(nw, size=min(nw, n_windows) - 1, replace=False)))
+    ntok = sum(pl["window_lengths"][w] for w in wins)
+    t0 = time.perf_counter()
+    oracle.forward_windows(feats, lens, P, cfg_d, wins)
+    dt = time.perf_counter() - t0
+    return {
+        "value": ntok / dt,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(wins)} windows ({ntok} tokens) of the {name} workload, windows {wins}: "
+                  f"conv stem, conv_out, {cfg_d['encoder_layers']} layers and projector in float64 numpy; "
+                  f"{dt:.1f} s wall",
+        "audio_s_per_s": ntok / 13.0 / dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wide", choices=list(si.WORKLOADS))
+    ap.add_argument("--cpu-windows", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time the steps without per-launch HIP events (no roofline)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the forward pass has no cross-GPU step here "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from packed_windowed_attention_amd import aut
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    name = args.workload
+    log(f"generating workload {name}")
+    cfg_d, lens, feats, P = si.workload(name)
+    dtype = cfg_d["dtype"]
+    cfg = aut.config(cfg_d)
+    dev = {k: torch.from_numpy(v).cuda() for k, v in P.items()}
+    packed = aut.weights_pack(cfg, dev, dtype)
+    del dev
+    fd = torch.from_numpy(feats).cuda()
+    pl = aut.plan(cfg, lens)
+    T = pl.total_tokens
+    audio_s = float(np.sum(lens)) / 100.0
+    ws = aut.workspace(cfg, pl, dtype)
+    out = torch.empty((T, cfg.output_dim), dtype=torch.float32, device="cuda")
+    log(f"T={T} tokens, {pl.n_windows} windows, {pl.n_chunks} chunks, workspace {ws.numel() / 2**30:.2f} GiB")
+
+    def step():
+        aut.encode(cfg, fd, lens, packed, dtype, out=out, ws=ws)
+
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    events = not args.no_kernel_events
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    if events:
+        aut.profile_collect()
+        aut.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        step()
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if events:
+        aut.profile_enable(False)
+        stats = aut.profile_collect()
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+
+    res = {
+        "metric": METRIC,
+        "value": T / (ms_per_step / 1000.0),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{name}: {DESCR[name]}",
+            "requests": int(len(lens)),
+            "total_tokens": int(T),
+            "audio_seconds": audio_s,
+            "n_windows": int(pl.n_windows),
+            "n_chunks": int(pl.n_chunks),
+            "parallelism": "single GPU",
+        },
+        "audio_s_per_s": audio_s / (ms_per_step / 1000.0),
+        "latency_ms": {q: float(np.percentile(step_ms, p)) for q, p in (("p50", 50), ("p95", 95), ("p99", 99))},
+    }
+    if events:
+        peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
+        kern = {}
+        for cls, s in stats.items():
+            if s["launches"] == 0:
+                continue
+            sec = s["total_ms"] / 1e3
+            kern[cls] = {"launches": s["launches"], "ms_per_step": s["total_ms"] / args.steps,
+                         "avg_us": 1e3 * s["total_ms"] / s["launches"],
+                         "tflops": s["flops"] / sec / 1e12 if sec else None,
+                         "gbs": s["bytes"] / sec / 1e9 if sec else None}
+        res["kernels"] = kern
+        g = stats["gemm"]
+        a = stats["attention"]
+        g_sec = g["total_ms"] / 1e3
+        res["roofline"] = {
+            "kernel": "gemm (qkv, out_proj, fc1, fc2, proj1, proj2)",
+            "bound": "mfma",
+            "achieved": g["flops"] / g_sec / 1e12,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": g["flops"] / g_sec / 1e12 / peak,
+            "traffic": None,
+            "flops_per_launch": g["flops"] / g["launches"],
+            "avg_launch_us": 1e6 * g_sec / g["launches"],
+        }
+        mf = [stats[c] for c in ("gemm", "attention")]
+        res["mfma_frac_gemm_attn"] = (sum(s["flops"] for s in mf) / (sum(s["total_ms"] for s in mf) / 1e3)
+                                      / 1e12 / peak)
+        allf = sum(s["flops"] for c, s in stats.items() if c != "layernorm")
+        res["mfma_frac_step"] = allf / args.steps / (ms_per_step / 1e3) / 1e12 / peak
+        res["attention_gbs"] = a["bytes"] / (a["total_ms"] / 1e3) / 1e9 if a["total_ms"] else None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on sampled windows)")
+        res["cpu_baseline"] = cpu_baseline(name, cfg_d, lens, feats, P, args.cpu_windows)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

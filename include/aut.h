@@ -1,0 +1,242 @@
+/*
+ * aut.h -- C ABI of the AuT audio-encoder forward pass on MI355X (gfx950).
+ *
+ * The encoder: a 128-bin log-mel at 100 frames/s is cut into 1 s chunks of
+ * 2 * n_window frames, each chunk goes through three stride-2 Conv2d + GELU
+ * layers and a linear conv_out, gets the chunk-local sinusoidal positions,
+ * and the valid tokens of every chunk are packed into one
+ * [total_tokens, d_model] sequence; a pre-LN stack of LayerNorm-with-bias
+ * encoder layers attends bidirectionally inside windows of n_window_infer
+ * frames (8 s -> 104 tokens) and a final LayerNorm + Linear/GELU/Linear
+ * projector maps every token to output_dim.  Sources: "mstar.model.
+ * components.aut_encoder" (m-star API page, module summary and the
+ * AuTEncoder / AuTEncoderConfig / AuTLayout entries) and "1A - AuT Audio
+ * Encoder" (openarchlab course, sections 1 and 3).
+ *
+ * Conventions for every call below:
+ *  - Every function returns aut_status; AUT_OK is 0.  On any other value
+ *    aut_last_error() returns a message for the calling thread.  No C++
+ *    exception crosses this interface.
+ *  - "device" pointers are HIP device memory on the current device; "host"
+ *    pointers are ordinary host memory.  The caller owns every buffer
+ *    (features, parameters, packed parameters, workspace, outputs) and the
+ *    stream.  The library never allocates or frees device memory and never
+ *    synchronises the device, except where a call says so.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - All argument checks happen before the first launch: a call that fails
+ *    validation has enqueued nothing.
+ *  - A batch without tokens (B = 0, or every length 0) is valid: the forward
+ *    calls enqueue nothing and need no device buffers (they may be NULL).
+ *  - Asynchronous faults of launched work surface as AUT_ERR_HIP from a later
+ *    call (or from the caller's own synchronisation).
+ */
+#ifndef AUT_H_
+#define AUT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AUT_OK = 0,
+  AUT_ERR_INVALID_ARG = 1,         /* NULL handle/pointer, negative or too long length, bad dtype */
+  AUT_ERR_UNSUPPORTED = 2,         /* a configuration the kernels do not implement */
+  AUT_ERR_MISSING_WEIGHT = 3,      /* a required parameter pointer is NULL (message names it) */
+  AUT_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace or destination smaller than required */
+  AUT_ERR_HIP = 5                  /* a HIP runtime call failed */
+} aut_status;
+
+/* Arithmetic type of the matrix products.  AUT_FP32: every operand and every
+ * activation is fp32.  AUT_BF16: GEMM/conv/attention operands are bf16
+ * (round to nearest even), accumulation, LayerNorm statistics, softmax and
+ * the residual stream stay fp32. */
+typedef enum { AUT_FP32 = 0, AUT_BF16 = 1 } aut_dtype;
+
+/* Model hyper-parameters.  Field names and defaults follow AuTEncoderConfig
+ * on the m-star API page; ln_eps and conv_out_bias are additions (LayerNorm
+ * epsilon 1e-5, conv_out without bias by default).
+ * Supported: num_mel_bins = 128; d_model = 64 * encoder_attention_heads,
+ * d_model a multiple of 64 and <= 2048; n_window_infer a multiple of
+ * 2 * n_window; tokens per window <= 128; downsample_hidden_size a multiple
+ * of 8; encoder_ffn_dim and output_dim multiples of 8. */
+typedef struct {
+  int32_t d_model;                /* 1024 */
+  int32_t encoder_layers;         /* 24 */
+  int32_t encoder_attention_heads;/* 16 */
+  int32_t encoder_ffn_dim;        /* 4096 */
+  int32_t num_mel_bins;           /* 128 */
+  int32_t n_window;               /* 50: a chunk is 2 * n_window frames */
+  int32_t n_window_infer;         /* 800 frames per attention window */
+  int32_t conv_chunksize;         /* 500: chunks per conv-stem batch (memory only) */
+  int32_t downsample_hidden_size; /* 480: conv channels C */
+  int32_t output_dim;             /* 2048 */
+  int32_t max_source_positions;   /* 1500: sinusoid table length */
+  int32_t conv_out_bias;          /* 0: conv_out has no bias; 1: it has one */
+  float ln_eps;                   /* 1e-5 */
+} aut_config;
+
+/* One chunk of the plan: which request it belongs to, its first mel frame,
+ * how many frames of it are real (<= 2 * n_window), how many tokens it keeps,
+ * and the packed row of its first token. */
+typedef struct {
+  int32_t request;
+  int32_t frame0;
+  int32_t valid_frames;
+  int32_t valid_tokens;
+  int32_t row0;
+} aut_chunk;
+
+typedef struct aut_plan aut_plan_t;
+
+/* Parameters as produced by a PyTorch-layout model, all fp32 *device*
+ * pointers: conv weights [C_out, C_in, 3, 3] (conv1: C_in = 1), linear
+ * weights [out, in].  Per-layer fields are *host* arrays holding
+ * encoder_layers device pointers each.  qkv_w stacks the q, k and v
+ * projections row-wise ([3 d, d], rows q then k then v), as the m-star page's
+ * fused qkv_proj does.  Every pointer is required except conv_out_b, which is
+ * read only when conv_out_bias = 1. */
+typedef struct {
+  const float* conv1_w;  const float* conv1_b;
+  const float* conv2_w;  const float* conv2_b;
+  const float* conv3_w;  const float* conv3_b;
+  const float* conv_out_w; const float* conv_out_b;   /* [d, C * 16], index c * 16 + f */
+  const float* const* ln1_g; const float* const* ln1_b;
+  const float* const* qkv_w; const float* const* qkv_b;
+  const float* const* o_w;   const float* const* o_b;
+  const float* const* ln2_g; const float* const* ln2_b;
+  const float* const* fc1_w; const float* const* fc1_b;
+  const float* const* fc2_w; const float* const* fc2_b;
+  const float* ln_post_g; const float* ln_post_b;
+  const float* proj1_w; const float* proj1_b;          /* [d, d] */
+  const float* proj2_w; const float* proj2_b;          /* [output_dim, d] */
+} aut_weight_ptrs;
+
+/* Fills *cfg with the AuTEncoderConfig defaults (m-star API page). */
+aut_status aut_config_default(aut_config* cfg);
+
+/* Checks a configuration against what the kernels implement
+ * (AUT_ERR_UNSUPPORTED with a reason otherwise). */
+aut_status aut_config_check(const aut_config* cfg);
+
+/* Host-only layout of one packed forward (m-star AuTEncoder.layout and
+ * tokens_for_frames / window_lengths): per request, ceil(L / chunk) chunks,
+ * tokens = three ceiling halvings of each chunk's valid frames (13 for a full
+ * 100-frame chunk), windows of window_tokens (104) then the remainder; windows
+ * never span requests; packed rows ordered request, chunk, token.
+ * feature_lens: host int32[B], each >= 0 (0 = an empty request with no
+ * tokens and no window).  B >= 0.  Never touches the GPU.  The handle is
+ * library-owned host memory, freed by aut_plan_destroy. */
+aut_status aut_plan(const aut_config* cfg, const int32_t* feature_lens, int32_t B,
+                    aut_plan_t** out);
+
+/* Sizes of a plan; any output pointer may be NULL. */
+aut_status aut_plan_counts(const aut_plan_t* plan, int64_t* total_tokens, int32_t* n_windows,
+                           int32_t* n_chunks);
+
+/* Copies a plan into host arrays; any may be NULL.  tokens_per_request:
+ * int32[B]; cu_seqlens: int32[n_windows + 1] (window starts, then the total);
+ * chunks: aut_chunk[n_chunks]. */
+aut_status aut_plan_copy(const aut_plan_t* plan, int32_t* tokens_per_request, int32_t* cu_seqlens,
+                         aut_chunk* chunks);
+
+void aut_plan_destroy(aut_plan_t* plan);
+
+/* Bytes of the packed-parameter buffer for (cfg, dtype). */
+aut_status aut_weights_bytes(const aut_config* cfg, aut_dtype dtype, size_t* bytes);
+
+/* Converts PyTorch-layout fp32 parameters into the kernels' layout and dtype
+ * in the caller's device buffer `dst` (aut_weights_bytes bytes), and computes
+ * the sinusoid position table into it (positions are computed, never loaded:
+ * cubic.dev wiki, "Positional Embeddings").  A NULL required pointer gives
+ * AUT_ERR_MISSING_WEIGHT naming the field (the m-star load_weights refuses to
+ * leave a parameter unloaded).  Asynchronous on `stream`; the sources must
+ * stay valid until the stream has passed this work. */
+aut_status aut_weights_pack(const aut_config* cfg, const aut_weight_ptrs* src, aut_dtype dtype,
+                            void* dst, size_t dst_bytes, void* stream);
+
+/* Device workspace bytes a forward of `plan` needs (plan tables, conv-stem
+ * batch buffers, residual stream and layer activations). */
+aut_status aut_workspace_bytes(const aut_config* cfg, const aut_plan_t* plan, aut_dtype dtype,
+                               size_t* bytes);
+
+/* Copies the plan's tables into the workspace (asynchronous H2D on
+ * `stream`).  The plan must not be destroyed before the stream has passed
+ * this copy.  Must precede aut_encode_planned / aut_frontend / aut_encode_packed
+ * with the same plan and workspace; it is the step kept outside a captured
+ * graph (the m-star page builds the attention plan outside the graph). */
+aut_status aut_plan_upload(const aut_plan_t* plan, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* The whole forward (m-star AuTEncoder.forward): plan, upload, frontend,
+ * encoder stack, projector.
+ * features: device fp32 [B, num_mel_bins, T_max], time fastest; frames at or
+ *   past feature_lens[b] are never read (treated as zero).
+ * feature_lens: host int32[B], 0 <= L <= T_max.
+ * packed: the aut_weights_pack buffer of the same cfg and dtype.
+ * out: device fp32 [total_tokens, output_dim], packed row order.
+ * workspace: device, >= aut_workspace_bytes for this batch.
+ * Synchronises `stream` once, after the plan upload, so the temporary plan can
+ * be freed; everything else is asynchronous. */
+aut_status aut_encode(const aut_config* cfg, const float* features, int32_t T_max,
+                      const int32_t* feature_lens, int32_t B, const void* packed, aut_dtype dtype,
+                      float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Kernels only, for a plan already uploaded into `workspace`: no allocation,
+ * no synchronisation, no host-to-device copy, so it can be captured in a HIP
+ * graph and replayed.  Arguments as aut_encode. */
+aut_status aut_encode_planned(const aut_config* cfg, const aut_plan_t* plan, const float* features,
+                              int32_t T_max, const void* packed, aut_dtype dtype, float* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* The frontend alone (m-star AuTEncoder.frontend): features -> packed chunk
+ * embeddings with positions, hidden: device fp32 [total_tokens, d_model].
+ * Requires the plan uploaded into `workspace`. */
+aut_status aut_frontend(const aut_config* cfg, const aut_plan_t* plan, const float* features,
+                        int32_t T_max, const void* packed, aut_dtype dtype, float* hidden,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* The layer stack and projector over a packed sequence (m-star
+ * AuTEncoder.encode): hidden device fp32 [total_tokens, d_model] (read only)
+ * -> out device fp32 [total_tokens, output_dim], attention blocks from the
+ * plan's cu_seqlens.  Requires the plan uploaded into `workspace`. */
+aut_status aut_encode_packed(const aut_config* cfg, const aut_plan_t* plan, const float* hidden,
+                             const void* packed, aut_dtype dtype, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Kernel classes for the optional per-launch timing below. */
+typedef enum {
+  AUT_K_CONV1 = 0,     /* conv1 (+GELU), fp32 vector ALU */
+  AUT_K_CONV_GEMM = 1, /* conv2 / conv3 implicit GEMM (+bias, GELU) */
+  AUT_K_CONV_OUT = 2,  /* conv_out GEMM (+bias, positions, pack) */
+  AUT_K_LAYERNORM = 3, /* LayerNorm rows -> GEMM operand */
+  AUT_K_GEMM = 4,      /* qkv / out_proj / fc1 / fc2 / proj1 / proj2 */
+  AUT_K_ATTENTION = 5, /* window attention */
+  AUT_K_COUNT = 6
+} aut_kernel_class;
+
+typedef struct {
+  int64_t launches;
+  double total_ms;  /* summed launch durations from HIP events around each launch */
+  double flops;     /* algorithmic flops of those launches (valid work only) */
+  double bytes;     /* algorithmic HBM bytes of those launches (each operand once) */
+} aut_kernel_stats;
+
+/* Turns per-launch timing on (1) or off (0).  While on, every launch is
+ * bracketed by two HIP events recorded on the launch's own stream. */
+aut_status aut_profile_enable(int on);
+
+/* Waits for the recorded events, adds their durations into
+ * stats[AUT_K_COUNT] (overwritten), and clears the records. */
+aut_status aut_profile_collect(aut_kernel_stats* stats);
+
+/* Message describing the last non-OK status returned on this thread. */
+const char* aut_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AUT_H_ */

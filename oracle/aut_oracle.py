@@ -24,8 +24,7 @@ What it follows (the pages are cited by title and section):
 * "Audio Encoder Component" (cubic.dev wiki), Transformer Encoder Layers:
   LayerNorm with bias (not RMSNorm); sinusoidal positions computed, not loaded.
 
-Readings where the pages are silent (listed with reasons in the repository's
-design notes): Whisper-style [sin | cos] table with increment
+Readings where the pages are silent: Whisper-style [sin | cos] table with increment
 ln(10000)/(d/2 - 1); chunk-local positions 0..k-1; exact (erf) GELU after each
 conv, fc1 and proj1; LayerNorm eps 1e-5 with population variance; pre-LN
 residual order; attention scale 1/sqrt(head_dim); flatten index c*16 + f;

@@ -1,0 +1,293 @@
+"""Python binding of libaut.so (the C ABI in include/aut.h).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+library.  PyTorch provides device memory and the stream.  There is no CPU
+fallback: if the library cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_char_p, c_double, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libaut.so")
+
+AUT_OK = 0
+STATUS = {0: "AUT_OK", 1: "AUT_ERR_INVALID_ARG", 2: "AUT_ERR_UNSUPPORTED",
+          3: "AUT_ERR_MISSING_WEIGHT", 4: "AUT_ERR_WORKSPACE_TOO_SMALL", 5: "AUT_ERR_HIP"}
+DTYPES = {"fp32": 0, "bf16": 1}
+KERNEL_CLASSES = ["conv1", "conv_gemm", "conv_out", "layernorm", "gemm", "attention"]
+
+CONFIG_FIELDS = ["d_model", "encoder_layers", "encoder_attention_heads", "encoder_ffn_dim",
+                 "num_mel_bins", "n_window", "n_window_infer", "conv_chunksize",
+                 "downsample_hidden_size", "output_dim", "max_source_positions", "conv_out_bias"]
+
+
+class AutConfig(ctypes.Structure):
+    _fields_ = [(f, c_int32) for f in CONFIG_FIELDS] + [("ln_eps", c_float)]
+
+
+class AutChunk(ctypes.Structure):
+    _fields_ = [("request", c_int32), ("frame0", c_int32), ("valid_frames", c_int32),
+                ("valid_tokens", c_int32), ("row0", c_int32)]
+
+
+_SCALAR_W = ["conv1_w", "conv1_b", "conv2_w", "conv2_b", "conv3_w", "conv3_b",
+             "conv_out_w", "conv_out_b"]
+LAYER_W = ["ln1_g", "ln1_b", "qkv_w", "qkv_b", "o_w", "o_b", "ln2_g", "ln2_b",
+           "fc1_w", "fc1_b", "fc2_w", "fc2_b"]
+_TAIL_W = ["ln_post_g", "ln_post_b", "proj1_w", "proj1_b", "proj2_w", "proj2_b"]
+
+
+class AutWeightPtrs(ctypes.Structure):
+    _fields_ = ([(n, c_void_p) for n in _SCALAR_W] + [(n, POINTER(c_void_p)) for n in LAYER_W]
+                + [(n, c_void_p) for n in _TAIL_W])
+
+
+class AutKernelStats(ctypes.Structure):
+    _fields_ = [("launches", c_int64), ("total_ms", c_double), ("flops", c_double), ("bytes", c_double)]
+
+
+# name -> (restype, argtypes); the exported symbols of include/aut.h
+SIGNATURES = {
+    "aut_config_default": (c_int, [POINTER(AutConfig)]),
+    "aut_config_check": (c_int, [POINTER(AutConfig)]),
+    "aut_plan": (c_int, [POINTER(AutConfig), POINTER(c_int32), c_int32, POINTER(c_void_p)]),
+    "aut_plan_counts": (c_int, [c_void_p, POINTER(c_int64), POINTER(c_int32), POINTER(c_int32)]),
+    "aut_plan_copy": (c_int, [c_void_p, POINTER(c_int32), POINTER(c_int32), POINTER(AutChunk)]),
+    "aut_plan_destroy": (None, [c_void_p]),
+    "aut_weights_bytes": (c_int, [POINTER(AutConfig), c_int, POINTER(c_size_t)]),
+    "aut_weights_pack": (c_int, [POINTER(AutConfig), POINTER(AutWeightPtrs), c_int, c_void_p,
+                                 c_size_t, c_void_p]),
+    "aut_workspace_bytes": (c_int, [POINTER(AutConfig), c_void_p, c_int, POINTER(c_size_t)]),
+    "aut_plan_upload": (c_int, [c_void_p, c_void_p, c_size_t, c_void_p]),
+    "aut_encode": (c_int, [POINTER(AutConfig), c_void_p, c_int32, POINTER(c_int32), c_int32,
+                           c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "aut_encode_planned": (c_int, [POINTER(AutConfig), c_void_p, c_void_p, c_int32, c_void_p,
+                                   c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "aut_frontend": (c_int, [POINTER(AutConfig), c_void_p, c_void_p, c_int32, c_void_p, c_int,
+                             c_void_p, c_void_p, c_size_t, c_void_p]),
+    "aut_encode_packed": (c_int, [POINTER(AutConfig), c_void_p, c_void_p, c_void_p, c_int,
+                                  c_void_p, c_void_p, c_size_t, c_void_p]),
+    "aut_profile_enable": (c_int, [c_int]),
+    "aut_profile_collect": (c_int, [POINTER(AutKernelStats)]),
+    "aut_last_error": (c_char_p, []),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libaut.so (built first if it is not there yet)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build
+            _build.build()
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+class AutError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def _check(st: int):
+    if st != AUT_OK:
+        msg = lib().aut_last_error()
+        raise AutError(st, msg.decode() if msg else "")
+
+
+def _dtype(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    return DTYPES[dtype]
+
+
+def config(cfg: dict | None = None, **over) -> AutConfig:
+    """aut_config from the library defaults, then a dict of AuTEncoderConfig
+    fields (unknown keys ignored), then keyword overrides."""
+    c = AutConfig()
+    _check(lib().aut_config_default(byref(c)))
+    src = dict(cfg or {})
+    src.update(over)
+    for f in CONFIG_FIELDS:
+        if f in src:
+            setattr(c, f, int(src[f]))
+    if "ln_eps" in src:
+        c.ln_eps = float(src["ln_eps"])
+    return c
+
+
+def config_check(cfg: AutConfig):
+    _check(lib().aut_config_check(byref(cfg)))
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return c_void_p(t.data_ptr()) if t is not None else c_void_p(0)
+
+
+class Plan:
+    """Owner of an aut_plan_t handle (host memory, freed with the object)."""
+
+    def __init__(self, cfg: AutConfig, feature_lens):
+        lens = [int(x) for x in feature_lens]
+        arr = (c_int32 * max(1, len(lens)))(*lens)
+        h = c_void_p()
+        _check(lib().aut_plan(byref(cfg), arr, len(lens), byref(h)))
+        self.handle = h
+        self.cfg = cfg
+        self.B = len(lens)
+        tot, nw, nc = c_int64(), c_int32(), c_int32()
+        _check(lib().aut_plan_counts(h, byref(tot), byref(nw), byref(nc)))
+        self.total_tokens, self.n_windows, self.n_chunks = tot.value, nw.value, nc.value
+
+    def copy(self):
+        """(tokens_per_request, cu_seqlens, chunks as list of 5-tuples)."""
+        tpr = (c_int32 * max(1, self.B))()
+        cu = (c_int32 * (self.n_windows + 1))()
+        ch = (AutChunk * max(1, self.n_chunks))()
+        _check(lib().aut_plan_copy(self.handle, tpr, cu, ch))
+        chunks = [(c.request, c.frame0, c.valid_frames, c.valid_tokens, c.row0)
+                  for c in ch[:self.n_chunks]]
+        return list(tpr[:self.B]), list(cu), chunks
+
+    @property
+    def cu_seqlens(self):
+        return self.copy()[1]
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h and _lib is not None:
+            _lib.aut_plan_destroy(h)
+            self.handle = None
+
+
+def plan(cfg: AutConfig, feature_lens) -> Plan:
+    """aut_plan: host-only layout of one packed forward."""
+    return Plan(cfg, feature_lens)
+
+
+def weights_bytes(cfg: AutConfig, dtype) -> int:
+    n = c_size_t()
+    _check(lib().aut_weights_bytes(byref(cfg), _dtype(dtype), byref(n)))
+    return n.value
+
+
+def weights_pack(cfg: AutConfig, params: dict, dtype, device="cuda", stream=None):
+    """aut_weights_pack: fp32 PyTorch-layout device tensors (names as in
+    synth_inputs.param_shapes) -> a packed uint8 device tensor.  Missing names
+    are passed as NULL so that the library reports them."""
+    import torch
+    L = cfg.encoder_layers
+    w = AutWeightPtrs()
+    keep = []
+    for n in _SCALAR_W + _TAIL_W:
+        t = params.get(n)
+        setattr(w, n, t.data_ptr() if t is not None else None)
+    for n in LAYER_W:
+        arr = (c_void_p * max(1, L))()
+        for i in range(L):
+            t = params.get(f"layers.{i}.{n}")
+            arr[i] = t.data_ptr() if t is not None else None
+        keep.append(arr)
+        setattr(w, n, ctypes.cast(arr, POINTER(c_void_p)))
+    nbytes = weights_bytes(cfg, dtype)
+    out = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    sp = _stream_ptr(stream)
+    _check(lib().aut_weights_pack(byref(cfg), byref(w), _dtype(dtype), _ptr(out), nbytes, sp))
+    # the sources only need to live until the pack kernels have read them
+    (stream or torch.cuda.current_stream()).synchronize()
+    return out
+
+
+def workspace_bytes(cfg: AutConfig, pl: Plan, dtype) -> int:
+    n = c_size_t()
+    _check(lib().aut_workspace_bytes(byref(cfg), pl.handle, _dtype(dtype), byref(n)))
+    return n.value
+
+
+def workspace(cfg: AutConfig, pl: Plan, dtype, device="cuda"):
+    import torch
+    return torch.empty(max(1, workspace_bytes(cfg, pl, dtype)), dtype=torch.uint8, device=device)
+
+
+def plan_upload(pl: Plan, ws, stream=None):
+    _check(lib().aut_plan_upload(pl.handle, _ptr(ws), ws.numel(), _stream_ptr(stream)))
+
+
+def _check_features(features):
+    if features.dtype.is_floating_point is False or str(features.dtype) != "torch.float32":
+        raise TypeError("features must be float32")
+    if features.dim() != 3 or not features.is_contiguous():
+        raise ValueError("features must be a contiguous [B, mel, T_max] tensor")
+
+
+def encode(cfg: AutConfig, features, feature_lens, packed, dtype, out=None, ws=None, stream=None):
+    """aut_encode: the whole forward; returns (out [T, output_dim] fp32, plan)."""
+    import torch
+    _check_features(features)
+    pl = Plan(cfg, feature_lens)
+    if out is None:
+        out = torch.empty((pl.total_tokens, cfg.output_dim), dtype=torch.float32, device=features.device)
+    if ws is None:
+        ws = workspace(cfg, pl, dtype, device=features.device)
+    lens = [int(x) for x in feature_lens]
+    arr = (c_int32 * max(1, len(lens)))(*lens)
+    _check(lib().aut_encode(byref(cfg), _ptr(features), features.shape[2], arr, len(lens),
+                            _ptr(packed), _dtype(dtype), _ptr(out), _ptr(ws), ws.numel(),
+                            _stream_ptr(stream)))
+    return out, pl
+
+
+def encode_planned(cfg: AutConfig, pl: Plan, features, packed, dtype, out, ws, stream=None):
+    """aut_encode_planned: kernels only, for a plan already uploaded into ws."""
+    _check_features(features)
+    _check(lib().aut_encode_planned(byref(cfg), pl.handle, _ptr(features), features.shape[2],
+                                    _ptr(packed), _dtype(dtype), _ptr(out), _ptr(ws), ws.numel(),
+                                    _stream_ptr(stream)))
+    return out
+
+
+def frontend(cfg: AutConfig, pl: Plan, features, packed, dtype, hidden, ws, stream=None):
+    """aut_frontend: features -> packed hidden [T, d_model] fp32 (plan uploaded)."""
+    _check_features(features)
+    _check(lib().aut_frontend(byref(cfg), pl.handle, _ptr(features), features.shape[2],
+                              _ptr(packed), _dtype(dtype), _ptr(hidden), _ptr(ws), ws.numel(),
+                              _stream_ptr(stream)))
+    return hidden
+
+
+def encode_packed(cfg: AutConfig, pl: Plan, hidden, packed, dtype, out, ws, stream=None):
+    """aut_encode_packed: layer stack + projector over packed hidden (plan uploaded)."""
+    _check(lib().aut_encode_packed(byref(cfg), pl.handle, _ptr(hidden), _ptr(packed),
+                                   _dtype(dtype), _ptr(out), _ptr(ws), ws.numel(),
+                                   _stream_ptr(stream)))
+    return out
+
+
+def profile_enable(on: bool):
+    _check(lib().aut_profile_enable(1 if on else 0))
+
+
+def profile_collect() -> dict:
+    """{class name: dict(launches, total_ms, flops, bytes)} since the last collect."""
+    st = (AutKernelStats * len(KERNEL_CLASSES))()
+    _check(lib().aut_profile_collect(st))
+    return {n: dict(launches=s.launches, total_ms=s.total_ms, flops=s.flops, bytes=s.bytes)
+            for n, s in zip(KERNEL_CLASSES, st)}

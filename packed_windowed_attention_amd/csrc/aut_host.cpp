@@ -1,0 +1,824 @@
+// Host layer of the AuT encoder library: configuration checks, the plan
+// (m-star AuTEncoder.layout), parameter packing, workspace layout, the
+// launch sequence of one forward, and optional per-launch event timing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "aut_internal.h"
+
+namespace {
+
+thread_local char g_err[1024] = "";
+
+aut_status fail(aut_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+#define HIPCHK(expr)                                                                      \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess) return fail(AUT_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int half_up(int n) { return (n + 1) / 2; }  // Conv2d(k3, s2, p1) output length
+
+size_t esize(aut_dtype dt) { return dt == AUT_BF16 ? 2 : 4; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// plan
+// ---------------------------------------------------------------------------
+
+struct aut_plan {
+  aut_config cfg;
+  aut::Geometry geo;
+  int32_t B = 0;
+  std::vector<int32_t> lens;
+  std::vector<int32_t> tokens_per_request;
+  std::vector<aut_chunk> chunks;
+  std::vector<int32_t> rowmap;   // per packed row: chunk * tokens_per_chunk + j
+  std::vector<int32_t> cu;       // n_windows + 1
+  std::vector<int32_t> worder;   // windows, longest first (ties by index)
+  int64_t total = 0;
+  double sum_len2 = 0;           // sum over windows of L^2
+};
+
+namespace aut {
+
+Geometry geometry(const aut_config& c) {
+  Geometry g;
+  g.mel = c.num_mel_bins;
+  g.cf = 2 * c.n_window;
+  g.h1 = half_up(g.mel);
+  g.w1 = half_up(g.cf);
+  g.h2 = half_up(g.h1);
+  g.w2 = half_up(g.w1);
+  g.h3 = half_up(g.h2);
+  g.w3 = half_up(g.w2);
+  g.C = c.downsample_hidden_size;
+  g.d = c.d_model;
+  g.H = c.encoder_attention_heads;
+  g.hd = g.H > 0 ? g.d / g.H : 0;
+  g.F = c.encoder_ffn_dim;
+  g.out = c.output_dim;
+  g.layers = c.encoder_layers;
+  g.chunks_per_window = g.cf > 0 ? c.n_window_infer / g.cf : 0;
+  g.window_tokens = g.w3 * g.chunks_per_window;
+  return g;
+}
+
+// ---------------------------------------------------------------------------
+// per-launch timing
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct ProfRecord {
+  hipEvent_t start, stop;
+  aut_kernel_class cls;
+  double flops, bytes;
+};
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+hipEvent_t g_pending_start = nullptr;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+void prof_begin(hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return;
+  g_pending_start = take_event();
+  if (g_pending_start) (void)hipEventRecord(g_pending_start, s);
+}
+
+void prof_end(hipStream_t s, aut_kernel_class cls, double flops, double bytes) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on || !g_pending_start) return;
+  hipEvent_t stop = take_event();
+  if (!stop) return;
+  (void)hipEventRecord(stop, s);
+  g_prof.push_back(ProfRecord{g_pending_start, stop, cls, flops, bytes});
+  g_pending_start = nullptr;
+}
+
+}  // namespace aut
+
+using aut::Geometry;
+
+// ---------------------------------------------------------------------------
+// configuration
+// ---------------------------------------------------------------------------
+
+extern "C" aut_status aut_config_default(aut_config* cfg) {
+  if (!cfg) return fail(AUT_ERR_INVALID_ARG, "cfg is NULL");
+  cfg->d_model = 1024;
+  cfg->encoder_layers = 24;
+  cfg->encoder_attention_heads = 16;
+  cfg->encoder_ffn_dim = 4096;
+  cfg->num_mel_bins = 128;
+  cfg->n_window = 50;
+  cfg->n_window_infer = 800;
+  cfg->conv_chunksize = 500;
+  cfg->downsample_hidden_size = 480;
+  cfg->output_dim = 2048;
+  cfg->max_source_positions = 1500;
+  cfg->conv_out_bias = 0;
+  cfg->ln_eps = 1e-5f;
+  return AUT_OK;
+}
+
+extern "C" aut_status aut_config_check(const aut_config* c) {
+  if (!c) return fail(AUT_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->encoder_layers < 0 || c->d_model <= 0 || c->encoder_attention_heads <= 0 ||
+      c->encoder_ffn_dim <= 0 || c->num_mel_bins <= 0 || c->n_window <= 0 ||
+      c->n_window_infer <= 0 || c->conv_chunksize <= 0 || c->downsample_hidden_size <= 0 ||
+      c->output_dim <= 0 || c->max_source_positions <= 0)
+    return fail(AUT_ERR_INVALID_ARG, "configuration sizes must be positive");
+  if (!(c->ln_eps > 0.f)) return fail(AUT_ERR_INVALID_ARG, "ln_eps must be positive");
+  if (c->conv_out_bias != 0 && c->conv_out_bias != 1)
+    return fail(AUT_ERR_INVALID_ARG, "conv_out_bias must be 0 or 1");
+  Geometry g = aut::geometry(*c);
+  if (c->num_mel_bins != 128) return fail(AUT_ERR_UNSUPPORTED, "num_mel_bins must be 128");
+  if (g.cf > 256) return fail(AUT_ERR_UNSUPPORTED, "2 * n_window must be <= 256");
+  if (c->n_window_infer % g.cf)
+    return fail(AUT_ERR_UNSUPPORTED, "n_window_infer (%d) must be a multiple of 2 * n_window (%d)",
+                c->n_window_infer, g.cf);
+  if (g.window_tokens > 128)
+    return fail(AUT_ERR_UNSUPPORTED, "tokens per window (%d) must be <= 128", g.window_tokens);
+  if (c->d_model != 64 * c->encoder_attention_heads)
+    return fail(AUT_ERR_UNSUPPORTED, "head_dim must be 64 (d_model = 64 * heads)");
+  if (c->d_model > 2048) return fail(AUT_ERR_UNSUPPORTED, "d_model must be <= 2048");
+  if (g.C % 8 || g.C > 1024)
+    return fail(AUT_ERR_UNSUPPORTED, "downsample_hidden_size must be a multiple of 8, <= 1024");
+  if (c->encoder_ffn_dim % 8 || c->output_dim % 8)
+    return fail(AUT_ERR_UNSUPPORTED, "encoder_ffn_dim and output_dim must be multiples of 8");
+  if (c->max_source_positions < g.w3)
+    return fail(AUT_ERR_UNSUPPORTED, "max_source_positions must cover the tokens of one chunk");
+  if (c->conv_chunksize > 8192) return fail(AUT_ERR_UNSUPPORTED, "conv_chunksize must be <= 8192");
+  return AUT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// plan
+// ---------------------------------------------------------------------------
+
+static const int64_t kMaxRows = 8000000;
+
+extern "C" aut_status aut_plan(const aut_config* cfg, const int32_t* feature_lens, int32_t B,
+                               aut_plan_t** out) {
+  if (!out) return fail(AUT_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  aut_status st = aut_config_check(cfg);
+  if (st != AUT_OK) return st;
+  if (B < 0) return fail(AUT_ERR_INVALID_ARG, "B must be >= 0");
+  if (B > 0 && !feature_lens) return fail(AUT_ERR_INVALID_ARG, "feature_lens is NULL");
+  for (int b = 0; b < B; ++b)
+    if (feature_lens[b] < 0) return fail(AUT_ERR_INVALID_ARG, "feature_lens[%d] = %d < 0", b, feature_lens[b]);
+
+  aut_plan_t* p = new (std::nothrow) aut_plan_t();
+  if (!p) return fail(AUT_ERR_INVALID_ARG, "out of host memory");
+  p->cfg = *cfg;
+  p->geo = aut::geometry(*cfg);
+  const Geometry& g = p->geo;
+  p->B = B;
+  p->lens.assign(feature_lens, feature_lens + B);
+  p->cu.push_back(0);
+  int64_t row = 0;
+  for (int b = 0; b < B; ++b) {
+    const int L = feature_lens[b];
+    const int nch = (L + g.cf - 1) / g.cf;
+    int64_t treq = 0;
+    for (int c = 0; c < nch; ++c) {
+      const int vf = std::min(g.cf, L - c * g.cf);
+      // tokens kept: the length of three stride-2 halvings of the valid frames
+      const int vt = half_up(half_up(half_up(vf)));
+      aut_chunk ch{b, c * g.cf, vf, vt, (int32_t)row};
+      const int32_t cid = (int32_t)p->chunks.size();
+      p->chunks.push_back(ch);
+      for (int j = 0; j < vt; ++j) p->rowmap.push_back(cid * g.w3 + j);
+      row += vt;
+      treq += vt;
+      if (row > kMaxRows) {
+        delete p;
+        return fail(AUT_ERR_UNSUPPORTED, "more than %lld tokens in one batch", (long long)kMaxRows);
+      }
+    }
+    p->tokens_per_request.push_back((int32_t)treq);
+    // windows: full windows of window_tokens, then the remainder
+    for (int64_t s = 0; s < treq; s += g.window_tokens) {
+      const int64_t len = std::min<int64_t>(g.window_tokens, treq - s);
+      p->cu.push_back(p->cu.back() + (int32_t)len);
+      p->sum_len2 += (double)len * (double)len;
+    }
+  }
+  p->total = row;
+  const int nw = (int)p->cu.size() - 1;
+  p->worder.resize(nw);
+  for (int w = 0; w < nw; ++w) p->worder[w] = w;
+  std::stable_sort(p->worder.begin(), p->worder.end(), [&](int a, int b) {
+    return (p->cu[a + 1] - p->cu[a]) > (p->cu[b + 1] - p->cu[b]);
+  });
+  *out = p;
+  return AUT_OK;
+}
+
+extern "C" aut_status aut_plan_counts(const aut_plan_t* plan, int64_t* total_tokens,
+                                      int32_t* n_windows, int32_t* n_chunks) {
+  if (!plan) return fail(AUT_ERR_INVALID_ARG, "plan is NULL");
+  if (total_tokens) *total_tokens = plan->total;
+  if (n_windows) *n_windows = (int32_t)plan->cu.size() - 1;
+  if (n_chunks) *n_chunks = (int32_t)plan->chunks.size();
+  return AUT_OK;
+}
+
+extern "C" aut_status aut_plan_copy(const aut_plan_t* plan, int32_t* tokens_per_request,
+                                    int32_t* cu_seqlens, aut_chunk* chunks) {
+  if (!plan) return fail(AUT_ERR_INVALID_ARG, "plan is NULL");
+  if (tokens_per_request && plan->B)
+    memcpy(tokens_per_request, plan->tokens_per_request.data(), sizeof(int32_t) * plan->B);
+  if (cu_seqlens) memcpy(cu_seqlens, plan->cu.data(), sizeof(int32_t) * plan->cu.size());
+  if (chunks && !plan->chunks.empty())
+    memcpy(chunks, plan->chunks.data(), sizeof(aut_chunk) * plan->chunks.size());
+  return AUT_OK;
+}
+
+extern "C" void aut_plan_destroy(aut_plan_t* plan) { delete plan; }
+
+// ---------------------------------------------------------------------------
+// packed parameters
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct LayerOff {
+  size_t ln1_g, ln1_b, qkv_w, qkv_b, o_w, o_b, ln2_g, ln2_b, fc1_w, fc1_b, fc2_w, fc2_b;
+};
+
+struct PackLayout {
+  size_t conv1_w, conv1_b, conv2_w, conv2_b, conv3_w, conv3_b, conv_out_w, conv_out_b, pe;
+  std::vector<LayerOff> layers;
+  size_t ln_post_g, ln_post_b, proj1_w, proj1_b, proj2_w, proj2_b;
+  size_t total;
+};
+
+PackLayout pack_layout(const Geometry& g, aut_dtype dt) {
+  PackLayout L;
+  size_t off = 0;
+  const size_t es = esize(dt);
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t C = g.C, d = g.d, F = g.F, O = g.out;
+  L.conv1_w = take(C * 9 * 4);
+  L.conv1_b = take(C * 4);
+  L.conv2_w = take(C * 9 * C * es);
+  L.conv2_b = take(C * 4);
+  L.conv3_w = take(C * 9 * C * es);
+  L.conv3_b = take(C * 4);
+  L.conv_out_w = take(d * g.h3 * C * es);
+  L.conv_out_b = take(d * 4);
+  L.pe = take((size_t)g.w3 * d * 4);
+  L.layers.resize(g.layers);
+  for (int i = 0; i < g.layers; ++i) {
+    LayerOff& l = L.layers[i];
+    l.ln1_g = take(d * 4);
+    l.ln1_b = take(d * 4);
+    l.qkv_w = take(3 * d * d * es);
+    l.qkv_b = take(3 * d * 4);
+    l.o_w = take(d * d * es);
+    l.o_b = take(d * 4);
+    l.ln2_g = take(d * 4);
+    l.ln2_b = take(d * 4);
+    l.fc1_w = take(F * d * es);
+    l.fc1_b = take(F * 4);
+    l.fc2_w = take(d * F * es);
+    l.fc2_b = take(d * 4);
+  }
+  L.ln_post_g = take(d * 4);
+  L.ln_post_b = take(d * 4);
+  L.proj1_w = take(d * d * es);
+  L.proj1_b = take(d * 4);
+  L.proj2_w = take(O * d * es);
+  L.proj2_b = take(O * 4);
+  L.total = off;
+  return L;
+}
+
+bool valid_dtype(aut_dtype dt) { return dt == AUT_FP32 || dt == AUT_BF16; }
+
+}  // namespace
+
+extern "C" aut_status aut_weights_bytes(const aut_config* cfg, aut_dtype dtype, size_t* bytes) {
+  aut_status st = aut_config_check(cfg);
+  if (st != AUT_OK) return st;
+  if (!valid_dtype(dtype)) return fail(AUT_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!bytes) return fail(AUT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = pack_layout(aut::geometry(*cfg), dtype).total;
+  return AUT_OK;
+}
+
+extern "C" aut_status aut_weights_pack(const aut_config* cfg, const aut_weight_ptrs* w,
+                                       aut_dtype dt, void* dst, size_t dst_bytes, void* stream) {
+  aut_status st = aut_config_check(cfg);
+  if (st != AUT_OK) return st;
+  if (!valid_dtype(dt)) return fail(AUT_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (!w) return fail(AUT_ERR_INVALID_ARG, "weights is NULL");
+  if (!dst) return fail(AUT_ERR_INVALID_ARG, "dst is NULL");
+  const Geometry g = aut::geometry(*cfg);
+  const PackLayout L = pack_layout(g, dt);
+  if (dst_bytes < L.total)
+    return fail(AUT_ERR_WORKSPACE_TOO_SMALL, "packed buffer has %zu bytes, needs %zu", dst_bytes,
+                L.total);
+
+  // every parameter must be present before anything is launched
+#define NEED(ptr, name)                                                       \
+  do {                                                                        \
+    if (!(ptr)) return fail(AUT_ERR_MISSING_WEIGHT, "missing parameter %s", name); \
+  } while (0)
+  NEED(w->conv1_w, "conv1_w"); NEED(w->conv1_b, "conv1_b");
+  NEED(w->conv2_w, "conv2_w"); NEED(w->conv2_b, "conv2_b");
+  NEED(w->conv3_w, "conv3_w"); NEED(w->conv3_b, "conv3_b");
+  NEED(w->conv_out_w, "conv_out_w");
+  if (cfg->conv_out_bias) NEED(w->conv_out_b, "conv_out_b");
+  NEED(w->ln_post_g, "ln_post_g"); NEED(w->ln_post_b, "ln_post_b");
+  NEED(w->proj1_w, "proj1_w"); NEED(w->proj1_b, "proj1_b");
+  NEED(w->proj2_w, "proj2_w"); NEED(w->proj2_b, "proj2_b");
+  if (g.layers > 0) {
+    NEED(w->ln1_g, "ln1_g"); NEED(w->ln1_b, "ln1_b"); NEED(w->qkv_w, "qkv_w"); NEED(w->qkv_b, "qkv_b");
+    NEED(w->o_w, "o_w"); NEED(w->o_b, "o_b"); NEED(w->ln2_g, "ln2_g"); NEED(w->ln2_b, "ln2_b");
+    NEED(w->fc1_w, "fc1_w"); NEED(w->fc1_b, "fc1_b"); NEED(w->fc2_w, "fc2_w"); NEED(w->fc2_b, "fc2_b");
+  }
+  char nm[64];
+  for (int i = 0; i < g.layers; ++i) {
+#define NEEDL(f)                                                                           \
+  do {                                                                                     \
+    if (!w->f[i]) {                                                                        \
+      snprintf(nm, sizeof(nm), "layers.%d.%s", i, #f);                                     \
+      return fail(AUT_ERR_MISSING_WEIGHT, "missing parameter %s", nm);                     \
+    }                                                                                      \
+  } while (0)
+    NEEDL(ln1_g); NEEDL(ln1_b); NEEDL(qkv_w); NEEDL(qkv_b); NEEDL(o_w); NEEDL(o_b);
+    NEEDL(ln2_g); NEEDL(ln2_b); NEEDL(fc1_w); NEEDL(fc1_b); NEEDL(fc2_w); NEEDL(fc2_b);
+#undef NEEDL
+  }
+#undef NEED
+
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)dst;
+  auto vec = [&](const float* src, size_t off, int n) {
+    return aut::launch_pack(src, base + off, AUT_FP32, aut::PACK_CAST, 1, n, 0, 0, s);
+  };
+  auto mat = [&](const float* src, size_t off, int rows, int cols) {
+    return aut::launch_pack(src, base + off, dt, aut::PACK_CAST, rows, cols, 0, 0, s);
+  };
+  const int C = g.C, d = g.d, F = g.F;
+  HIPCHK(aut::launch_pack(w->conv1_w, base + L.conv1_w, AUT_FP32, aut::PACK_CAST, C, 9, 0, 0, s));
+  HIPCHK(vec(w->conv1_b, L.conv1_b, C));
+  HIPCHK(aut::launch_pack(w->conv2_w, base + L.conv2_w, dt, aut::PACK_CONV, C, 9 * C, C, 0, s));
+  HIPCHK(vec(w->conv2_b, L.conv2_b, C));
+  HIPCHK(aut::launch_pack(w->conv3_w, base + L.conv3_w, dt, aut::PACK_CONV, C, 9 * C, C, 0, s));
+  HIPCHK(vec(w->conv3_b, L.conv3_b, C));
+  HIPCHK(aut::launch_pack(w->conv_out_w, base + L.conv_out_w, dt, aut::PACK_CONV_OUT, d,
+                          g.h3 * C, C, g.h3, s));
+  if (cfg->conv_out_bias) HIPCHK(vec(w->conv_out_b, L.conv_out_b, d));
+  HIPCHK(aut::launch_pe_table((float*)(base + L.pe), g.w3, d, s));
+  for (int i = 0; i < g.layers; ++i) {
+    const LayerOff& l = L.layers[i];
+    HIPCHK(vec(w->ln1_g[i], l.ln1_g, d));
+    HIPCHK(vec(w->ln1_b[i], l.ln1_b, d));
+    HIPCHK(mat(w->qkv_w[i], l.qkv_w, 3 * d, d));
+    HIPCHK(vec(w->qkv_b[i], l.qkv_b, 3 * d));
+    HIPCHK(mat(w->o_w[i], l.o_w, d, d));
+    HIPCHK(vec(w->o_b[i], l.o_b, d));
+    HIPCHK(vec(w->ln2_g[i], l.ln2_g, d));
+    HIPCHK(vec(w->ln2_b[i], l.ln2_b, d));
+    HIPCHK(mat(w->fc1_w[i], l.fc1_w, F, d));
+    HIPCHK(vec(w->fc1_b[i], l.fc1_b, F));
+    HIPCHK(mat(w->fc2_w[i], l.fc2_w, d, F));
+    HIPCHK(vec(w->fc2_b[i], l.fc2_b, d));
+  }
+  HIPCHK(vec(w->ln_post_g, L.ln_post_g, d));
+  HIPCHK(vec(w->ln_post_b, L.ln_post_b, d));
+  HIPCHK(mat(w->proj1_w, L.proj1_w, d, d));
+  HIPCHK(vec(w->proj1_b, L.proj1_b, d));
+  HIPCHK(mat(w->proj2_w, L.proj2_w, g.out, d));
+  HIPCHK(vec(w->proj2_b, L.proj2_b, g.out));
+  return AUT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// workspace
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct WsLayout {
+  size_t chunks, rowmap, cu, worder;
+  size_t a1, a2, a3;
+  size_t x, xn, qkv, o, h;
+  size_t total;
+  int nb;  // chunks per conv-stem batch
+};
+
+WsLayout ws_layout(const aut_plan_t& p, aut_dtype dt) {
+  const Geometry& g = p.geo;
+  WsLayout W;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t es = esize(dt);
+  const size_t T = (size_t)p.total;
+  const size_t nch = p.chunks.size();
+  const size_t nw = p.cu.size() - 1;
+  W.nb = (int)std::min<size_t>((size_t)p.cfg.conv_chunksize, nch);
+  const size_t nb = (size_t)W.nb;
+  W.chunks = take(nch * sizeof(aut_chunk));
+  W.rowmap = take(T * 4);
+  W.cu = take((nw + 1) * 4);
+  W.worder = take(nw * 4);
+  W.a1 = take(nb * g.h1 * g.w1 * g.C * es);
+  W.a2 = take(nb * g.h2 * g.w2 * g.C * es);
+  W.a3 = take(nb * g.h3 * g.w3 * g.C * es);
+  W.x = take(T * g.d * 4);
+  W.xn = take(T * g.d * es);
+  W.qkv = take(T * 3 * g.d * es);
+  W.o = take(T * g.d * es);
+  W.h = take(T * std::max(g.F, g.d) * es);
+  W.total = off;
+  return W;
+}
+
+aut_status check_common(const aut_config* cfg, const aut_plan_t* plan, aut_dtype dt,
+                        const void* packed, void* ws, size_t ws_bytes, WsLayout* W) {
+  aut_status st = aut_config_check(cfg);
+  if (st != AUT_OK) return st;
+  if (!plan) return fail(AUT_ERR_INVALID_ARG, "plan is NULL");
+  if (!valid_dtype(dt)) return fail(AUT_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (memcmp(cfg, &plan->cfg, sizeof(aut_config)) != 0)
+    return fail(AUT_ERR_INVALID_ARG, "plan was made for a different configuration");
+  *W = ws_layout(*plan, dt);
+  if (plan->total > 0) {
+    if (!packed) return fail(AUT_ERR_MISSING_WEIGHT, "packed parameters are NULL");
+    if (!ws) return fail(AUT_ERR_INVALID_ARG, "workspace is NULL");
+  }
+  if (plan->total > 0 && ws_bytes < W->total)
+    return fail(AUT_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes,
+                W->total);
+  return AUT_OK;
+}
+
+}  // namespace
+
+extern "C" aut_status aut_workspace_bytes(const aut_config* cfg, const aut_plan_t* plan,
+                                          aut_dtype dtype, size_t* bytes) {
+  aut_status st = aut_config_check(cfg);
+  if (st != AUT_OK) return st;
+  if (!plan) return fail(AUT_ERR_INVALID_ARG, "plan is NULL");
+  if (!valid_dtype(dtype)) return fail(AUT_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!bytes) return fail(AUT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ws_layout(*plan, dtype).total;
+  return AUT_OK;
+}
+
+extern "C" aut_status aut_plan_upload(const aut_plan_t* plan, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  if (!plan) return fail(AUT_ERR_INVALID_ARG, "plan is NULL");
+  const WsLayout W = ws_layout(*plan, AUT_FP32);  // table offsets do not depend on dtype
+  const size_t need = W.worder + plan->worder.size() * 4;
+  if (plan->total == 0) return AUT_OK;
+  if (!ws) return fail(AUT_ERR_INVALID_ARG, "workspace is NULL");
+  if (ws_bytes < need) return fail(AUT_ERR_WORKSPACE_TOO_SMALL, "workspace too small for the plan");
+  hipStream_t s = (hipStream_t)stream;
+  char* b = (char*)ws;
+  HIPCHK(hipMemcpyAsync(b + W.chunks, plan->chunks.data(), plan->chunks.size() * sizeof(aut_chunk),
+                        hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(b + W.rowmap, plan->rowmap.data(), plan->rowmap.size() * 4,
+                        hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(b + W.cu, plan->cu.data(), plan->cu.size() * 4, hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(b + W.worder, plan->worder.data(), plan->worder.size() * 4,
+                        hipMemcpyHostToDevice, s));
+  return AUT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// the forward pass
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct Ctx {
+  const aut_plan_t* p;
+  const Geometry* g;
+  aut_dtype dt;
+  const PackLayout* P;
+  const WsLayout* W;
+  const char* pk;  // packed parameters
+  char* ws;        // workspace
+  hipStream_t s;
+};
+
+template <typename X>
+const X* pk_at(const Ctx& c, size_t off) { return reinterpret_cast<const X*>(c.pk + off); }
+
+aut_status gemm(const Ctx& c, aut_kernel_class cls, const aut::GemmArgs& a, int amode, int epi,
+                double bytes) {
+  aut::prof_begin(c.s);
+  hipError_t e = aut::launch_gemm(a, amode, epi, c.dt, c.s);
+  if (e != hipSuccess) return fail(AUT_ERR_HIP, "gemm launch failed: %s", hipGetErrorString(e));
+  aut::prof_end(c.s, cls, 2.0 * a.M * (double)a.N * a.K, bytes);
+  return AUT_OK;
+}
+
+aut::GemmArgs plain_args(const void* A, const void* B, int M, int N, int K, const float* bias,
+                         void* out, long ldo) {
+  aut::GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.A = A; a.lda = K; a.B = B; a.ldb = K;
+  a.M = M; a.N = N; a.K = K;
+  a.bias = bias; a.out = out; a.ldo = ldo;
+  return a;
+}
+
+// frontend: features -> hidden [T, d] fp32
+aut_status run_frontend(const Ctx& c, const float* feat, int T_max, float* hidden) {
+  const aut_plan_t& p = *c.p;
+  const Geometry& g = *c.g;
+  const WsLayout& W = *c.W;
+  const PackLayout& P = *c.P;
+  const size_t es = esize(c.dt);
+  const int nch = (int)p.chunks.size();
+  const int* d_chunks = (const int*)(c.ws + W.chunks);
+  const int* d_rowmap = (const int*)(c.ws + W.rowmap);
+  for (int c0 = 0; c0 < nch; c0 += W.nb) {
+    const int n = std::min(W.nb, nch - c0);
+    // conv1 + GELU
+    aut::prof_begin(c.s);
+    hipError_t e = aut::launch_conv1(feat, T_max, d_chunks, c0, n, pk_at<float>(c, P.conv1_w),
+                                     pk_at<float>(c, P.conv1_b), c.ws + W.a1, c.dt, g, c.s);
+    if (e != hipSuccess) return fail(AUT_ERR_HIP, "conv1 launch failed: %s", hipGetErrorString(e));
+    aut::prof_end(c.s, AUT_K_CONV1, 2.0 * 9 * g.C * (double)g.h1 * g.w1 * n,
+                  (double)n * g.mel * g.cf * 4 + (double)n * g.h1 * g.w1 * g.C * es);
+    // conv2, conv3: implicit GEMMs over the whole (padded) chunks
+    for (int layer = 2; layer <= 3; ++layer) {
+      aut::GemmArgs a;
+      memset(&a, 0, sizeof(a));
+      const bool l2 = layer == 2;
+      a.A = c.ws + (l2 ? W.a1 : W.a2);
+      a.B = c.pk + (l2 ? P.conv2_w : P.conv3_w);
+      a.ldb = 9 * g.C;
+      a.hin = l2 ? g.h1 : g.h2;
+      a.win = l2 ? g.w1 : g.w2;
+      a.hout = l2 ? g.h2 : g.h3;
+      a.wout = l2 ? g.w2 : g.w3;
+      a.cin = g.C;
+      a.xmajor = l2 ? 0 : 1;  // conv3 output stored [chunk][x][y][c] for the token flatten
+      a.M = n * a.hout * a.wout;
+      a.N = g.C;
+      a.K = 9 * g.C;
+      a.bias = pk_at<float>(c, l2 ? P.conv2_b : P.conv3_b);
+      a.out = c.ws + (l2 ? W.a2 : W.a3);
+      a.ldo = g.C;
+      const double bytes = ((double)n * a.hin * a.win * g.C + (double)g.C * a.K +
+                            (double)a.M * g.C) * es;
+      aut_status st = gemm(c, AUT_K_CONV_GEMM, a, aut::A_CONV, aut::EPI_STORE_GELU, bytes);
+      if (st != AUT_OK) return st;
+    }
+    // conv_out + positions over the batch's valid tokens
+    const int r0 = p.chunks[c0].row0;
+    const int r1 = (c0 + n < nch) ? p.chunks[c0 + n].row0 : (int)p.total;
+    if (r1 > r0) {
+      aut::GemmArgs a;
+      memset(&a, 0, sizeof(a));
+      a.A = c.ws + W.a3;
+      a.lda = (long)g.h3 * g.C;
+      a.B = c.pk + P.conv_out_w;
+      a.ldb = (long)g.h3 * g.C;
+      a.M = r1 - r0;
+      a.N = g.d;
+      a.K = g.h3 * g.C;
+      a.rowmap = d_rowmap + r0;
+      a.rowmap_base = c0 * g.w3;
+      a.tpc = g.w3;
+      a.bias = p.cfg.conv_out_bias ? pk_at<float>(c, P.conv_out_b) : nullptr;
+      a.out = hidden + (size_t)r0 * g.d;
+      a.ldo = g.d;
+      a.pe = pk_at<float>(c, P.pe);
+      const double bytes = ((double)a.M * a.K + (double)g.d * a.K) * es + (double)a.M * g.d * 4;
+      aut_status st = gemm(c, AUT_K_CONV_OUT, a, aut::A_ROWMAP, aut::EPI_PE, bytes);
+      if (st != AUT_OK) return st;
+    }
+  }
+  return AUT_OK;
+}
+
+aut_status layernorm(const Ctx& c, const float* x, size_t g_off, size_t b_off, void* y) {
+  const int T = (int)c.p->total, d = c.g->d;
+  aut::prof_begin(c.s);
+  hipError_t e = aut::launch_layernorm(x, pk_at<float>(c, g_off), pk_at<float>(c, b_off), y, T, d,
+                                       c.p->cfg.ln_eps, c.dt, c.s);
+  if (e != hipSuccess) return fail(AUT_ERR_HIP, "layernorm launch failed: %s", hipGetErrorString(e));
+  aut::prof_end(c.s, AUT_K_LAYERNORM, 8.0 * T * d, (double)T * d * (4 + esize(c.dt)));
+  return AUT_OK;
+}
+
+// encoder stack + projector: ws.x (fp32 residual, in place) -> out [T, out]
+aut_status run_encode(const Ctx& c, float* out) {
+  const aut_plan_t& p = *c.p;
+  const Geometry& g = *c.g;
+  const WsLayout& W = *c.W;
+  const PackLayout& P = *c.P;
+  const int T = (int)p.total;
+  if (T == 0) return AUT_OK;
+  const int d = g.d, F = g.F;
+  const double es = (double)esize(c.dt);
+  float* x = (float*)(c.ws + W.x);
+  void* xn = c.ws + W.xn;
+  void* qkv = c.ws + W.qkv;
+  void* o = c.ws + W.o;
+  void* h = c.ws + W.h;
+  aut_status st;
+  for (int i = 0; i < g.layers; ++i) {
+    const LayerOff& l = P.layers[i];
+    if ((st = layernorm(c, x, l.ln1_g, l.ln1_b, xn)) != AUT_OK) return st;
+    st = gemm(c, AUT_K_GEMM,
+              plain_args(xn, c.pk + l.qkv_w, T, 3 * d, d, pk_at<float>(c, l.qkv_b), qkv, 3 * d),
+              aut::A_PLAIN, aut::EPI_STORE, ((double)T * d + 3.0 * d * d + 3.0 * T * d) * es);
+    if (st != AUT_OK) return st;
+    aut::prof_begin(c.s);
+    hipError_t e = aut::launch_attention(qkv, o, (const int*)(c.ws + W.cu),
+                                         (const int*)(c.ws + W.worder), (int)p.cu.size() - 1, g.H,
+                                         d, c.dt, c.s);
+    if (e != hipSuccess) return fail(AUT_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+    aut::prof_end(c.s, AUT_K_ATTENTION, 4.0 * d * p.sum_len2, 4.0 * T * d * es);
+    st = gemm(c, AUT_K_GEMM, plain_args(o, c.pk + l.o_w, T, d, d, pk_at<float>(c, l.o_b), x, d),
+              aut::A_PLAIN, aut::EPI_RESID, ((double)T * d + (double)d * d) * es + 8.0 * T * d);
+    if (st != AUT_OK) return st;
+    if ((st = layernorm(c, x, l.ln2_g, l.ln2_b, xn)) != AUT_OK) return st;
+    st = gemm(c, AUT_K_GEMM, plain_args(xn, c.pk + l.fc1_w, T, F, d, pk_at<float>(c, l.fc1_b), h, F),
+              aut::A_PLAIN, aut::EPI_STORE_GELU, ((double)T * d + (double)F * d + (double)T * F) * es);
+    if (st != AUT_OK) return st;
+    st = gemm(c, AUT_K_GEMM, plain_args(h, c.pk + l.fc2_w, T, d, F, pk_at<float>(c, l.fc2_b), x, d),
+              aut::A_PLAIN, aut::EPI_RESID, ((double)T * F + (double)d * F) * es + 8.0 * T * d);
+    if (st != AUT_OK) return st;
+  }
+  if ((st = layernorm(c, x, P.ln_post_g, P.ln_post_b, xn)) != AUT_OK) return st;
+  st = gemm(c, AUT_K_GEMM, plain_args(xn, c.pk + P.proj1_w, T, d, d, pk_at<float>(c, P.proj1_b), h, d),
+            aut::A_PLAIN, aut::EPI_STORE_GELU, (2.0 * T * d + (double)d * d) * es);
+  if (st != AUT_OK) return st;
+  st = gemm(c, AUT_K_GEMM,
+            plain_args(h, c.pk + P.proj2_w, T, g.out, d, pk_at<float>(c, P.proj2_b), out, g.out),
+            aut::A_PLAIN, aut::EPI_STORE_F32,
+            ((double)T * d + (double)g.out * d) * es + 4.0 * T * g.out);
+  return st;
+}
+
+aut_status check_features(const float* features, int32_t T_max, const aut_plan_t& p) {
+  if (T_max < 0) return fail(AUT_ERR_INVALID_ARG, "T_max must be >= 0");
+  for (int b = 0; b < p.B; ++b)
+    if (p.lens[b] > T_max)
+      return fail(AUT_ERR_INVALID_ARG, "feature_lens[%d] = %d exceeds T_max = %d", b, p.lens[b], T_max);
+  if (p.total > 0 && !features) return fail(AUT_ERR_INVALID_ARG, "features is NULL");
+  return AUT_OK;
+}
+
+}  // namespace
+
+extern "C" aut_status aut_encode_planned(const aut_config* cfg, const aut_plan_t* plan,
+                                         const float* features, int32_t T_max, const void* packed,
+                                         aut_dtype dt, float* out, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  WsLayout W;
+  aut_status st = check_common(cfg, plan, dt, packed, ws, ws_bytes, &W);
+  if (st != AUT_OK) return st;
+  if ((st = check_features(features, T_max, *plan)) != AUT_OK) return st;
+  if (plan->total > 0 && !out) return fail(AUT_ERR_INVALID_ARG, "out is NULL");
+  if (plan->total == 0) return AUT_OK;
+  const PackLayout P = pack_layout(plan->geo, dt);
+  Ctx c{plan, &plan->geo, dt, &P, &W, (const char*)packed, (char*)ws, (hipStream_t)stream};
+  if ((st = run_frontend(c, features, T_max, (float*)((char*)ws + W.x))) != AUT_OK) return st;
+  return run_encode(c, out);
+}
+
+extern "C" aut_status aut_frontend(const aut_config* cfg, const aut_plan_t* plan,
+                                   const float* features, int32_t T_max, const void* packed,
+                                   aut_dtype dt, float* hidden, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  WsLayout W;
+  aut_status st = check_common(cfg, plan, dt, packed, ws, ws_bytes, &W);
+  if (st != AUT_OK) return st;
+  if ((st = check_features(features, T_max, *plan)) != AUT_OK) return st;
+  if (plan->total > 0 && !hidden) return fail(AUT_ERR_INVALID_ARG, "hidden is NULL");
+  if (plan->total == 0) return AUT_OK;
+  const PackLayout P = pack_layout(plan->geo, dt);
+  Ctx c{plan, &plan->geo, dt, &P, &W, (const char*)packed, (char*)ws, (hipStream_t)stream};
+  return run_frontend(c, features, T_max, hidden);
+}
+
+extern "C" aut_status aut_encode_packed(const aut_config* cfg, const aut_plan_t* plan,
+                                        const float* hidden, const void* packed, aut_dtype dt,
+                                        float* out, void* ws, size_t ws_bytes, void* stream) {
+  WsLayout W;
+  aut_status st = check_common(cfg, plan, dt, packed, ws, ws_bytes, &W);
+  if (st != AUT_OK) return st;
+  if (plan->total == 0) return AUT_OK;
+  if (!hidden || !out) return fail(AUT_ERR_INVALID_ARG, "hidden or out is NULL");
+  const PackLayout P = pack_layout(plan->geo, dt);
+  Ctx c{plan, &plan->geo, dt, &P, &W, (const char*)packed, (char*)ws, (hipStream_t)stream};
+  HIPCHK(hipMemcpyAsync((char*)ws + W.x, hidden, (size_t)plan->total * plan->geo.d * 4,
+                        hipMemcpyDeviceToDevice, c.s));
+  return run_encode(c, out);
+}
+
+extern "C" aut_status aut_encode(const aut_config* cfg, const float* features, int32_t T_max,
+                                 const int32_t* feature_lens, int32_t B, const void* packed,
+                                 aut_dtype dt, float* out, void* ws, size_t ws_bytes, void* stream) {
+  aut_plan_t* plan = nullptr;
+  aut_status st = aut_plan(cfg, feature_lens, B, &plan);
+  if (st != AUT_OK) return st;
+  WsLayout W;
+  st = check_common(cfg, plan, dt, packed, ws, ws_bytes, &W);
+  if (st == AUT_OK) st = check_features(features, T_max, *plan);
+  if (st == AUT_OK && plan->total > 0 && !out) st = fail(AUT_ERR_INVALID_ARG, "out is NULL");
+  if (st == AUT_OK) st = aut_plan_upload(plan, ws, ws_bytes, stream);
+  if (st == AUT_OK && plan->total > 0) {
+    // the copies read the plan's host memory: let them finish before it is freed
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) st = fail(AUT_ERR_HIP, "hipStreamSynchronize failed: %s", hipGetErrorString(e));
+  }
+  if (st == AUT_OK)
+    st = aut_encode_planned(cfg, plan, features, T_max, packed, dt, out, ws, ws_bytes, stream);
+  aut_plan_destroy(plan);
+  return st;
+}
+
+// ---------------------------------------------------------------------------
+// timing and errors
+// ---------------------------------------------------------------------------
+
+extern "C" aut_status aut_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(aut::g_prof_mu);
+  aut::g_prof_on = on != 0;
+  return AUT_OK;
+}
+
+extern "C" aut_status aut_profile_collect(aut_kernel_stats* stats) {
+  if (!stats) return fail(AUT_ERR_INVALID_ARG, "stats is NULL");
+  std::lock_guard<std::mutex> lk(aut::g_prof_mu);
+  for (int k = 0; k < AUT_K_COUNT; ++k) stats[k] = aut_kernel_stats{0, 0.0, 0.0, 0.0};
+  aut_status st = AUT_OK;
+  for (auto& r : aut::g_prof) {
+    if (st == AUT_OK) {
+      hipError_t e = hipEventSynchronize(r.stop);
+      float ms = 0.f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+      if (e != hipSuccess) {
+        st = fail(AUT_ERR_HIP, "event timing failed: %s", hipGetErrorString(e));
+      } else {
+        aut_kernel_stats& k = stats[r.cls];
+        k.launches += 1;
+        k.total_ms += ms;
+        k.flops += r.flops;
+        k.bytes += r.bytes;
+      }
+    }
+    aut::g_event_pool.push_back(r.start);
+    aut::g_event_pool.push_back(r.stop);
+  }
+  aut::g_prof.clear();
+  return st;
+}
+
+extern "C" const char* aut_last_error(void) { return g_err; }

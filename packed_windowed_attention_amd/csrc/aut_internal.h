@@ -1,0 +1,74 @@
+// Internal interfaces between the host layer (aut_host.cpp) and the kernel
+// launchers (*.hip).  Not part of the public C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/aut.h"
+
+namespace aut {
+
+// Geometry derived from a configuration.
+struct Geometry {
+  int mel;          // H0 = num_mel_bins
+  int cf;           // W0 = chunk frames = 2 * n_window
+  int h1, w1;       // conv1 output grid
+  int h2, w2;       // conv2 output grid
+  int h3, w3;       // conv3 output grid; w3 = tokens per full chunk
+  int C;            // conv channels
+  int d, H, hd, F, out;
+  int layers;
+  int window_tokens;
+  int chunks_per_window;
+};
+
+Geometry geometry(const aut_config& c);
+
+// Per-launch timing hooks (no-ops unless aut_profile_enable(1)).
+void prof_begin(hipStream_t s);
+void prof_end(hipStream_t s, aut_kernel_class cls, double flops, double bytes);
+
+// ------------------------------- kernels ---------------------------------
+
+// Weight packing.
+enum PackMode { PACK_CAST = 0, PACK_CONV = 1, PACK_CONV_OUT = 2 };
+hipError_t launch_pack(const float* src, void* dst, aut_dtype dt, int mode, int rows, int cols,
+                       int C, int F, hipStream_t s);
+hipError_t launch_pe_table(float* pe, int rows, int d, hipStream_t s);
+
+// conv1 + GELU over `nb` chunks starting at chunk_first of the plan.
+hipError_t launch_conv1(const float* feat, int T_max, const int* chunks, int chunk_first, int nb,
+                        const float* w1, const float* b1, void* a1, aut_dtype dt,
+                        const Geometry& g, hipStream_t s);
+
+// Generic MFMA GEMM: C[M, N] = A[M, K] * B[N, K]^T with an A-gather mode and
+// an epilogue.
+enum AMode { A_PLAIN = 0, A_CONV = 1, A_ROWMAP = 2 };
+enum Epi { EPI_STORE = 0, EPI_STORE_GELU = 1, EPI_RESID = 2, EPI_PE = 3, EPI_STORE_F32 = 4 };
+
+struct GemmArgs {
+  const void* A; long lda;
+  const void* B; long ldb;
+  int M, N, K;
+  // A_CONV: implicit-GEMM conv with 3x3 kernel, stride 2, pad 1.  Row m of A
+  // is output pixel (chunk, oy, ox), decomposed x-major or y-major.
+  int hin, win, hout, wout, cin, xmajor;
+  // A_ROWMAP: row m of A is A + (rowmap[m] - rowmap_base) * lda.
+  const int* rowmap; int rowmap_base; int tpc;
+  // epilogue
+  const float* bias;   // [N] or null
+  void* out; long ldo;
+  const float* pe;     // EPI_PE: [tpc, N] position rows, indexed rowmap[m] % tpc
+};
+hipError_t launch_gemm(const GemmArgs& a, int amode, int epi, aut_dtype dt, hipStream_t s);
+
+// LayerNorm rows of fp32 x [T, d] into the GEMM operand type.
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, int T, int d,
+                            float eps, aut_dtype dt, hipStream_t s);
+
+// Window attention: qkv [T, 3d] (q | k | v) -> o [T, d].
+hipError_t launch_attention(const void* qkv, void* o, const int* cu, const int* worder,
+                            int n_windows, int H, int d, aut_dtype dt, hipStream_t s);
+
+}  // namespace aut

@@ -1,0 +1,74 @@
+// Device helpers shared by the gfx950 kernels of the AuT encoder.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;  // one 16-byte unit
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+
+typedef __bf16 bf16_t;
+
+// Exact GELU, x * Phi(x), with the device library's erff ('gelu' activation of
+// AuTEncoderConfig; the erf form, not the tanh approximation).
+__device__ __forceinline__ float gelu_f(float x) {
+  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
+}
+
+// fp32 -> bf16, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ bf16_t to_bf16(float x) { return (bf16_t)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return to_bf16(x); }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return (float)x; }
+
+// Elements of T in one 16-byte unit.
+template <typename T> struct UnitElems { static constexpr int value = 16 / (int)sizeof(T); };
+
+// ---------------------------------------------------------------------------
+// 16x16 output tile, 32-deep k step, fp32 accumulate.
+//
+// Operand fragments: for a k step of 32, lane l (row or column l % 16, group
+// g = l / 16) supplies 8 k-values.  The k index each of the 8 slots stands for
+// may be any fixed function of (g, slot) as long as the A and B fragments use
+// the same one, since the product sums over all 32.  Result: lane l holds
+// C[4 g + r][l % 16], r = 0..3.
+//
+// bf16: one v_mfma_f32_16x16x32_bf16 (slots = the 8 packed bf16).
+// fp32: eight v_mfma_f32_16x16x4_f32, instruction s taking slot s of every
+//       lane, so that the four groups cover four distinct k per instruction.
+// ---------------------------------------------------------------------------
+struct FragBF16 { bf16x8_t v; };
+struct FragF32 { float v[8]; };
+
+template <typename T> struct FragOf;
+template <> struct FragOf<bf16_t> { typedef FragBF16 type; };
+template <> struct FragOf<float> { typedef FragF32 type; };
+
+__device__ __forceinline__ void mma16_k32(f32x4_t& acc, const FragBF16& a, const FragBF16& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16_k32(f32x4_t& acc, const FragF32& a, const FragF32& b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], acc, 0, 0, 0);
+}
+
+// Fragment from 16-byte units: bf16 needs one unit, fp32 two consecutive ones.
+__device__ __forceinline__ void frag_from_units(FragBF16& f, u32x4_t u0, u32x4_t) {
+  f.v = __builtin_bit_cast(bf16x8_t, u0);
+}
+__device__ __forceinline__ void frag_from_units(FragF32& f, u32x4_t u0, u32x4_t u1) {
+  f32x4_t a = __builtin_bit_cast(f32x4_t, u0), b = __builtin_bit_cast(f32x4_t, u1);
+  f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+  f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+}
+
+__device__ __forceinline__ u32x4_t zero_unit() { return u32x4_t{0u, 0u, 0u, 0u}; }
+
+__device__ __forceinline__ u32x4_t ldg_unit(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}

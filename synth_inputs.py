@@ -6,8 +6,9 @@ request lengths, the log-mel features and the parameters, and names the five
 workloads.  Everything the encoder computes lives on each side separately.
 
 Workloads (model sizes from the AuTEncoderConfig field list and defaults of the
-m-star ``aut_encoder`` API page; request length mixes are synthetic stand-ins
-for a read-speech test set, see the design doc of the repository):
+m-star ``aut_encoder`` API page; the request length mixes are synthetic
+stand-ins for a read-speech test set's utterance lengths, and N(-4, 2) noise
+stands in for real log-mel values):
 
 ====  =========================================  ==============================
 name  requests / lengths                         model
@@ -155,13 +156,14 @@ def round_to_bf16(a: np.ndarray) -> np.ndarray:
 
     Used only to prepare *inputs* (parameters) for bf16 workloads, so both the
     oracle and the device path start from the same representable values.
+    Finite inputs only (generated parameters are never NaN or Inf).
     """
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    u = (u + 0x7FFF + lsb) >> 16 << 16
-    out = u.astype(np.uint32).view(np.float32)
-    # NaN/Inf do not occur in generated parameters.
+    out = np.array(a, dtype=np.float32, copy=True)
+    u = out.view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
     return out
 
 

@@ -1,0 +1,154 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and its host-only calls (configuration, plan, sizes, argument
+checks) behave as documented.  No call here launches GPU work: every error
+path tested returns before the first launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth_inputs as si
+from packed_windowed_attention_amd import aut
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "aut.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:aut_status|void|const char\*)\s+(aut_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = aut.lib()
+    names = declared_functions()
+    assert len(names) == len(aut.SIGNATURES) == 17
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(aut.SIGNATURES), "binding and header disagree"
+
+
+def test_config_default_matches_page_defaults():
+    import json
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_values.json")))
+    d = gold["config_defaults"]["value"]
+    c = aut.config()
+    for k in aut.CONFIG_FIELDS:
+        if k in d:
+            assert getattr(c, k) == d[k], k
+    assert c.conv_out_bias == 0 and abs(c.ln_eps - 1e-5) < 1e-12
+
+
+@pytest.mark.parametrize("name", si.WORKLOADS)
+def test_plan_bit_exact_vs_oracle(name):
+    cfg_d = si.model_config(name)
+    lens = si.feature_lens(name)
+    pl = aut.plan(aut.config(cfg_d), lens)
+    tpr, cu, chunks = pl.copy()
+    op = oracle.plan(lens, cfg_d)
+    assert tpr == op["tokens_per_request"]
+    assert cu == op["cu_seqlens"]
+    assert chunks == [tuple(c) for c in op["chunks"]]
+    assert pl.total_tokens == op["total_tokens"]
+
+
+@pytest.mark.parametrize("lens", [[0], [1], [99, 100, 101], [0, 5, 0, 100, 0], list(range(0, 1700, 37)),
+                                  [120000], [800] * 3 + [801]])
+def test_plan_edge_cases_vs_oracle(lens):
+    cfg_d = si.model_config("rag")
+    pl = aut.plan(aut.config(cfg_d), lens)
+    tpr, cu, chunks = pl.copy()
+    op = oracle.plan(lens, cfg_d)
+    assert (tpr, cu, chunks) == (op["tokens_per_request"], op["cu_seqlens"], [tuple(c) for c in op["chunks"]])
+
+
+def test_plan_random_lengths_vs_oracle():
+    rng = np.random.default_rng(99)
+    cfg_d = si.model_config("wide")
+    for _ in range(20):
+        lens = rng.integers(0, 5000, size=rng.integers(1, 40))
+        pl = aut.plan(aut.config(cfg_d), lens)
+        tpr, cu, chunks = pl.copy()
+        op = oracle.plan(lens, cfg_d)
+        assert cu == op["cu_seqlens"] and tpr == op["tokens_per_request"]
+        assert chunks == [tuple(c) for c in op["chunks"]]
+
+
+def status_of(fn):
+    with pytest.raises(aut.AutError) as e:
+        fn()
+    return e.value.status
+
+
+def test_config_errors():
+    assert status_of(lambda: aut.config_check(aut.config(d_model=1000, encoder_attention_heads=16))) == 2
+    assert status_of(lambda: aut.config_check(aut.config(n_window_infer=750))) == 2
+    assert status_of(lambda: aut.config_check(aut.config(n_window_infer=1600))) == 2   # 208 tokens
+    assert status_of(lambda: aut.config_check(aut.config(num_mel_bins=80))) == 2
+    assert status_of(lambda: aut.config_check(aut.config(downsample_hidden_size=100))) == 2
+    assert status_of(lambda: aut.config_check(aut.config(d_model=0))) == 1
+    assert status_of(lambda: aut.plan(aut.config(), [100, -1])) == 1
+    assert status_of(lambda: aut.weights_bytes(aut.config(), 7)) == 1
+
+
+def test_sizes():
+    cfg = aut.config(si.model_config("wide"))
+    n_params = sum(int(np.prod(s)) for _, s in si.param_shapes(si.model_config("wide")))
+    wb = aut.weights_bytes(cfg, "bf16")
+    assert 2 * n_params <= wb <= 2 * n_params + 4 * 10 ** 7
+    assert aut.weights_bytes(cfg, "fp32") >= 4 * n_params
+    pl = aut.plan(cfg, si.feature_lens("wide"))
+    ws = aut.workspace_bytes(cfg, pl, "bf16")
+    T, d = pl.total_tokens, cfg.d_model
+    assert ws >= T * d * 4 + T * 3 * d * 2 + T * cfg.encoder_ffn_dim * 2
+
+
+def test_missing_weight_reported_before_launch():
+    cfg = aut.config(si.model_config("tiny"))
+    w = aut.AutWeightPtrs()
+    nbytes = aut.weights_bytes(cfg, "fp32")
+    st = aut.lib().aut_weights_pack(ctypes.byref(cfg), ctypes.byref(w), 0, ctypes.c_void_p(256),
+                                    nbytes, None)
+    assert st == 3
+    assert b"conv1_w" in aut.lib().aut_last_error()
+    # every scalar given but one per-layer entry missing: the message names it
+    for n in aut._SCALAR_W + aut._TAIL_W:
+        setattr(w, n, 4096)
+    arrs = []
+    for n in aut.LAYER_W:
+        arr = (ctypes.c_void_p * 1)(4096 if n != "fc2_b" else None)
+        arrs.append(arr)
+        setattr(w, n, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)))
+    st = aut.lib().aut_weights_pack(ctypes.byref(cfg), ctypes.byref(w), 0, ctypes.c_void_p(256),
+                                    nbytes, None)
+    assert st == 3 and b"layers.0.fc2_b" in aut.lib().aut_last_error()
+    # destination too small
+    st = aut.lib().aut_weights_pack(ctypes.byref(cfg), ctypes.byref(w), 0, ctypes.c_void_p(256),
+                                    nbytes - 1, None)
+    assert st == 4
+
+
+def test_encode_argument_checks_before_launch():
+    cfg = aut.config(si.model_config("tiny"))
+    lens = (ctypes.c_int32 * 2)(800, 900)
+    fake = ctypes.c_void_p(4096)
+    L = aut.lib()
+    # a length beyond T_max
+    st = L.aut_encode(ctypes.byref(cfg), fake, 850, lens, 2, fake, 0, fake, fake, 1 << 40, None)
+    assert st == 1 and b"T_max" in L.aut_last_error()
+    # workspace too small
+    st = L.aut_encode(ctypes.byref(cfg), fake, 900, lens, 2, fake, 0, fake, fake, 1024, None)
+    assert st == 4
+    # unknown dtype
+    st = L.aut_encode(ctypes.byref(cfg), fake, 900, lens, 2, fake, 5, fake, fake, 1 << 40, None)
+    assert st == 1
+    # a plan made for another configuration
+    pl = aut.plan(aut.config(si.model_config("rag")), [800])
+    st = L.aut_encode_planned(ctypes.byref(cfg), pl.handle, fake, 900, fake, 0, fake, fake, 1 << 40, None)
+    assert st == 1
+    # an empty batch is a no-op that needs no buffers at all
+    z = (ctypes.c_int32 * 1)(0)
+    assert L.aut_encode(ctypes.byref(cfg), None, 0, z, 1, None, 0, None, None, 0, None) == 0
+    assert L.aut_encode(ctypes.byref(cfg), None, 0, z, 0, None, 0, None, None, 0, None) == 0

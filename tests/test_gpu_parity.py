@@ -1,0 +1,182 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Stage-wise on a small ragged configuration (fp32 and bf16), then every named
+workload: the tiny fp32 one and the ragged bf16 one on their whole output,
+the three large bf16 ones on a seeded sample of windows that the oracle
+computes exactly (windows are independent end to end).
+Tolerances: fp32 max_i |g - r| / max(|r_i|, rms r) <= 1e-4; bf16 max-abs
+<= 2e-2 and per-token cosine >= 0.999; the plan is compared exactly.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth_inputs as si
+from gpu_common import (check, forward, pack, features_dev, sample_windows, small_cfg, torch_mod,
+                        workload)
+
+pytestmark = pytest.mark.gpu
+
+SMALL_LENS = np.array([250, 0, 800, 37, 1737, 5, 100, 101])
+
+
+def small_case(dtype, **kw):
+    cfg = small_cfg(dtype, **kw)
+    feats = si.mel_features(SMALL_LENS, seed=21)
+    P = si.params(cfg, seed=21, std=0.05)
+    return cfg, SMALL_LENS, feats, P
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_small_stages(dtype):
+    """frontend, encode and the whole forward separately."""
+    from packed_windowed_attention_amd import aut
+    torch = torch_mod()
+    cfg_d, lens, feats, P = small_case(dtype)
+    print(f"case: small {dtype} lens={list(lens)}", flush=True)
+    cfg, packed = pack(cfg_d, P)
+    pl = aut.plan(cfg, lens)
+    ws = aut.workspace(cfg, pl, dtype)
+    aut.plan_upload(pl, ws)
+    T = pl.total_tokens
+    hid = torch.empty((T, cfg_d["d_model"]), dtype=torch.float32, device="cuda")
+    aut.frontend(cfg, pl, features_dev(feats), packed, dtype, hid, ws)
+    torch.cuda.synchronize()
+    ref_hid, opl = oracle.frontend(feats, lens, P, cfg_d)
+    assert pl.copy()[1] == opl["cu_seqlens"]
+    check(hid.double().cpu().numpy(), ref_hid, dtype, "frontend")
+
+    out = torch.empty((T, cfg_d["output_dim"]), dtype=torch.float32, device="cuda")
+    aut.encode_packed(cfg, pl, torch.from_numpy(ref_hid.astype(np.float32)).cuda(), packed, dtype, out, ws)
+    torch.cuda.synchronize()
+    ref_enc = oracle.encode(ref_hid.astype(np.float32).astype(np.float64), opl["cu_seqlens"], P, cfg_d)
+    check(out.double().cpu().numpy(), ref_enc, dtype, "encode")
+
+    y, _ = forward(cfg_d, lens, feats, packed=packed, cfg=cfg)
+    ref, _ = oracle.forward(feats, lens, P, cfg_d)
+    check(y, ref, dtype, "forward")
+
+
+def test_small_conv_out_bias():
+    cfg_d, lens, feats, P = small_case("fp32")
+    cfg_d = dict(cfg_d, conv_out_bias=True)
+    P = si.params(cfg_d, seed=22, std=0.05)
+    y, _ = forward(cfg_d, lens, feats, P)
+    ref, _ = oracle.forward(feats, lens, P, cfg_d)
+    check(y, ref, "fp32", "conv_out bias")
+
+
+@pytest.mark.parametrize("lens", [[1], [7, 8, 9], [99, 100, 101], [800, 801, 1599, 1600, 1601]])
+def test_edge_lengths(lens):
+    cfg_d = small_cfg("fp32", encoder_layers=1)
+    lens = np.array(lens)
+    feats = si.mel_features(lens, seed=5)
+    P = si.params(cfg_d, seed=5, std=0.05)
+    y, pl = forward(cfg_d, lens, feats, P)
+    ref, opl = oracle.forward(feats, lens, P, cfg_d)
+    assert pl.copy()[1] == opl["cu_seqlens"]
+    check(y, ref, "fp32", f"lens {list(lens)}")
+
+
+def test_empty_batch():
+    from packed_windowed_attention_amd import aut
+    cfg_d = small_cfg("fp32", encoder_layers=1)
+    P = si.params(cfg_d, seed=1)
+    cfg, packed = pack(cfg_d, P)
+    feats = features_dev(si.mel_features([0, 0], seed=1))
+    out, pl = aut.encode(cfg, feats, [0, 0], packed, "fp32")
+    assert pl.total_tokens == 0 and out.shape[0] == 0
+
+
+def test_padding_contents_ignored():
+    """Buffer contents past each length (NaN, zeros, huge values) never matter."""
+    cfg_d, lens, _, P = small_case("bf16")
+    cfg, packed = pack(cfg_d, P)
+    outs = []
+    for pad, tmax in [(np.nan, None), (0.0, None), (1e30, 2000)]:
+        feats = si.mel_features(lens, seed=21, pad_value=pad, t_max=tmax)
+        y, _ = forward(cfg_d, lens, feats, packed=packed, cfg=cfg)
+        outs.append(y)
+    assert np.isfinite(outs[0]).all()
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_tiny_fp32():
+    """1 request of 8 s, 1 layer d 1280, C 128, fp32: whole output."""
+    cfg_d, lens, feats, P = workload("tiny")
+    print("case: tiny fp32", flush=True)
+    y, pl = forward(cfg_d, lens, feats, P)
+    ref, opl = oracle.forward(feats, lens, P, cfg_d)
+    assert pl.copy()[1] == opl["cu_seqlens"] == [0, 104]
+    check(y, ref, "fp32", "tiny")
+
+
+def test_rag_bf16():
+    """4 ragged requests, 18 layers d 1024: whole output."""
+    cfg_d, lens, feats, P = workload("rag")
+    print("case: rag bf16", flush=True)
+    y, pl = forward(cfg_d, lens, feats, P)
+    ref, opl = oracle.forward(feats, lens, P, cfg_d)
+    assert pl.copy()[1] == opl["cu_seqlens"]
+    check(y, ref, "bf16", "rag")
+
+
+@pytest.mark.parametrize("name", ["wide", "long", "conc"])
+def test_large_sampled_windows(name):
+    """Full-size bf16 forward; the oracle recomputes a seeded sample of windows."""
+    cfg_d, lens, feats, P = workload(name)
+    print(f"case: {name} bf16 full size, sampled windows", flush=True)
+    y, pl = forward(cfg_d, lens, feats, P)
+    opl = oracle.plan(lens, cfg_d)
+    assert pl.copy()[1] == opl["cu_seqlens"]
+    assert np.isfinite(y).all()
+    wins = sample_windows(opl, seed=si.workload_seed(name), n_random=1)
+    res = oracle.forward_windows(feats, lens, P, cfg_d, wins)
+    for w, (r0, ref) in res.items():
+        check(y[r0:r0 + ref.shape[0]], ref, "bf16", f"{name} window {w} (rows {r0}+{ref.shape[0]})")
+
+
+def test_window_isolation_bitwise():
+    """openarchlab "1A", section 4: change one window's spectrogram, every other
+    window's output must not move at all (0.00e+00)."""
+    cfg_d, lens, feats, P = workload("rag")
+    cfg, packed = pack(cfg_d, P)
+    y0, pl = forward(cfg_d, lens, feats, packed=packed, cfg=cfg)
+    cu = pl.copy()[1]
+    f2 = feats.copy()
+    f2[3, :, 800:1600] += 0.25   # request 3, window 1 (frames 800..1599)
+    y1, _ = forward(cfg_d, lens, f2, packed=packed, cfg=cfg)
+    changed = [w for w in range(len(cu) - 1) if not np.array_equal(y0[cu[w]:cu[w + 1]], y1[cu[w]:cu[w + 1]])]
+    target = 1 + 1 + 3 + 1          # windows of requests 0..2 come first (1 + 1 + 3)
+    assert changed == [target], changed
+    dev = max(np.abs(y0[cu[w]:cu[w + 1]] - y1[cu[w]:cu[w + 1]]).max() for w in range(len(cu) - 1) if w != target)
+    print(f"isolation: max deviation outside the perturbed window {dev:.2e}", flush=True)
+    assert dev == 0.0
+
+
+def test_run_twice_bitwise():
+    """Full-width workload twice: identical bits (no order-dependent reductions)."""
+    cfg_d, lens, feats, P = workload("wide")
+    cfg, packed = pack(cfg_d, P)
+    y0, _ = forward(cfg_d, lens, feats, packed=packed, cfg=cfg)
+    y1, _ = forward(cfg_d, lens, feats, packed=packed, cfg=cfg)
+    assert np.array_equal(y0, y1)
+
+
+def test_planned_matches_encode():
+    """aut_encode_planned after one aut_plan_upload equals aut_encode, also on
+    a second call (the plan is reused, as in a replayed graph)."""
+    from packed_windowed_attention_amd import aut
+    torch = torch_mod()
+    cfg_d, lens, feats, P = small_case("bf16")
+    cfg, packed = pack(cfg_d, P)
+    y, _ = forward(cfg_d, lens, feats, packed=packed, cfg=cfg)
+    pl = aut.plan(cfg, lens)
+    ws = aut.workspace(cfg, pl, "bf16")
+    aut.plan_upload(pl, ws)
+    fd = features_dev(feats)
+    for _ in range(2):
+        out = torch.full((pl.total_tokens, cfg_d["output_dim"]), float("nan"), device="cuda")
+        aut.encode_planned(cfg, pl, fd, packed, "bf16", out, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.double().cpu().numpy(), y)
