@@ -78,7 +78,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wide", choices=list(si.WORKLOADS))
-    ap.add_argument("--cpu-windows", type=int, default=3)
+    ap.add_argument("--cpu-windows", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without per-launch HIP events (no roofline)")

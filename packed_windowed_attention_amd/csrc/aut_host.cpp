@@ -463,7 +463,11 @@ WsLayout ws_layout(const aut_plan_t& p, aut_dtype dt) {
   const size_t T = (size_t)p.total;
   const size_t nch = p.chunks.size();
   const size_t nw = p.cu.size() - 1;
-  W.nb = (int)std::min<size_t>((size_t)p.cfg.conv_chunksize, nch);
+  // chunks per conv-stem batch: conv_chunksize, also kept small enough that
+  // the batch's conv1 output stays below 2 GiB (32-bit buffer offsets)
+  const size_t per_chunk = (size_t)g.h1 * g.w1 * g.C * es;
+  const size_t max_nb = std::max<size_t>(1, ((size_t)1 << 31) / per_chunk - 1);
+  W.nb = (int)std::min<size_t>(std::min<size_t>((size_t)p.cfg.conv_chunksize, nch), max_nb);
   const size_t nb = (size_t)W.nb;
   W.chunks = take(nch * sizeof(aut_chunk));
   W.rowmap = take(T * 4);
@@ -608,6 +612,7 @@ aut_status run_frontend(const Ctx& c, const float* feat, int T_max, float* hidde
       a.M = n * a.hout * a.wout;
       a.N = g.C;
       a.K = 9 * g.C;
+      a.a_bytes = (size_t)n * a.hin * a.win * g.C * es;
       a.bias = pk_at<float>(c, l2 ? P.conv2_b : P.conv3_b);
       a.out = c.ws + (l2 ? W.a2 : W.a3);
       a.ldo = g.C;
@@ -631,6 +636,7 @@ aut_status run_frontend(const Ctx& c, const float* feat, int T_max, float* hidde
       a.K = g.h3 * g.C;
       a.rowmap = d_rowmap + r0;
       a.rowmap_base = c0 * g.w3;
+      a.a_bytes = (size_t)n * g.w3 * g.h3 * g.C * es;
       a.tpc = g.w3;
       a.bias = p.cfg.conv_out_bias ? pk_at<float>(c, P.conv_out_b) : nullptr;
       a.out = hidden + (size_t)r0 * g.d;

@@ -56,12 +56,19 @@ struct GemmArgs {
   int hin, win, hout, wout, cin, xmajor;
   // A_ROWMAP: row m of A is A + (rowmap[m] - rowmap_base) * lda.
   const int* rowmap; int rowmap_base; int tpc;
+  // A_CONV / A_ROWMAP: bytes of the A buffer (every gathered offset is below;
+  // must be < 2^31 for the bf16 kernel's 32-bit buffer offsets)
+  size_t a_bytes;
   // epilogue
   const float* bias;   // [N] or null
   void* out; long ldo;
   const float* pe;     // EPI_PE: [tpc, N] position rows, indexed rowmap[m] % tpc
 };
+// bf16 runs the 256-row kernel (k_gemm256.hip), fp32 the 128 x 128 one
+// (k_gemm128.hip).
 hipError_t launch_gemm(const GemmArgs& a, int amode, int epi, aut_dtype dt, hipStream_t s);
+hipError_t launch_gemm128(const GemmArgs& a, int amode, int epi, aut_dtype dt, hipStream_t s);
+hipError_t launch_gemm256(const GemmArgs& a, int amode, int epi, hipStream_t s);
 
 // LayerNorm rows of fp32 x [T, d] into the GEMM operand type.
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, int T, int d,

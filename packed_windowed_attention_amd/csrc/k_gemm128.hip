@@ -1,4 +1,6 @@
-// MFMA GEMM for gfx950: C[M, N] = A[M, K] * B[N, K]^T (+ epilogue).
+// MFMA GEMM for gfx950, 128 x 128 tiles: C[M, N] = A[M, K] * B[N, K]^T (+ epilogue).
+// Used for the fp32 mode (eight fp32 MFMAs per 32-deep step); the bf16 mode
+// runs the 256-row kernel in k_gemm256.hip.
 //
 // Both operands are k-contiguous (B is a PyTorch [out, in] weight), which is
 // the natural operand order of the matrix cores: every lane fetches 8
@@ -221,7 +223,7 @@ hipError_t dispatch(const GemmArgs& a, int amode, int epi, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& a, int amode, int epi, aut_dtype dt, hipStream_t s) {
+hipError_t launch_gemm128(const GemmArgs& a, int amode, int epi, aut_dtype dt, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (dt == AUT_BF16) return dispatch<bf16_t>(a, amode, epi, s);
   return dispatch<float>(a, amode, epi, s);

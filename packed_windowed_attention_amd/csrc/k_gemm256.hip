@@ -1,0 +1,390 @@
+// bf16 MFMA GEMM for gfx950 with 256-row block tiles:
+// C[M, N] = A[M, K] * B[N, K]^T (+ epilogue), fp32 accumulation.
+//
+// Block tile 256 x BN (BN = 160 or 128), 4 waves in a 2 x 2 grid, each wave
+// 128 x BN/2; the accumulators (160 or 128 per lane) live in the accumulation
+// registers, one wave per SIMD.  (A 256 x 256 tile needs all 256 accumulation
+// registers and the compiler then spills; it is not offered.)
+//
+// Operands go from memory straight into LDS (buffer_load_dwordx4 ... lds), no
+// registers in between, through a ring of three k-steps of 64 bf16 (128 bytes
+// per tile row; 156 KiB for BN = 160); loads run two steps ahead of the matrix instructions and each
+// step needs one barrier.  A buffer load whose offset lies past the end of its
+// buffer returns zero, which gives the zero padding of tile tails (rows past M
+// or N, k past K) and of the convolution's border taps for free.  Within a
+// 128-byte row the eight 16-byte units are XOR-swizzled by row & 7, which the
+// LDS conflict counters show to be conflict-free for the fragment loads (a
+// 64-byte-row layout doubled the cycles of every fragment load).
+//
+// The weight fragment is the matrix instruction's first operand and the
+// activation fragment its second, so each lane ends up with four consecutive
+// output columns of one row: the epilogue stores 8 (bf16) or 16 (fp32) bytes
+// per lane and reads bias, residual and position rows as float4.
+//
+// Tiles are ordered for the 8 XCDs (each with its own L2): workgroup b runs on
+// XCD b % 8, so XCD x is given the contiguous tile range
+// [x * per_xcd, (x + 1) * per_xcd), walked 8 M-tiles per N column, so the 32
+// tiles an XCD runs at once share 8 A panels and 4 B panels.
+//
+// A-gather modes: plain; implicit 3x3 stride-2 pad-1 convolution over a
+// channels-last activation, k = tap * C + c (openarchlab "1A", section 3:
+// Conv2d(k=3, s=2, p=1)); row map (conv_out over the valid tokens).
+// Epilogues: bias then store, GELU then store, residual add into fp32,
+// position add, fp32 store.
+#include "aut_internal.h"
+#include "device_common.h"
+
+namespace aut {
+
+namespace {
+
+constexpr int BM = 256;
+constexpr int NTHR = 256;
+constexpr int KU = 8;       // 16-byte units per row per k step
+constexpr int BK = 64;      // bf16 per row per k step
+constexpr int GROUP_M = 8;
+constexpr unsigned OOB = 0x80000000u;  // an offset past every buffer here: loads zero
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz(int unit, int row) { return unit ^ (row & 7); }
+
+// LDS destination of a direct load, as a wave-uniform address with its origin
+// hidden from the compiler: ordering against the fragment reads is kept by the
+// explicit vmcnt waits and barriers below, and the compiler then does not add
+// a wait for every load in flight before each fragment read.
+// The low 32 bits of a flat address inside the LDS aperture are the LDS offset.
+__device__ __forceinline__ lds_void* dma_dst(const u32x4_t* p) {
+  const unsigned a = (unsigned)(size_t)p;
+  return (lds_void*)(size_t)__builtin_amdgcn_readfirstlane(a);
+}
+
+__device__ __forceinline__ void store4(bf16_t* p, const float (&v)[4]) {
+  const bf16_t b0 = to_bf16(v[0]), b1 = to_bf16(v[1]), b2 = to_bf16(v[2]), b3 = to_bf16(v[3]);
+  const unsigned int lo = (unsigned int)__builtin_bit_cast(unsigned short, b0) |
+                          ((unsigned int)__builtin_bit_cast(unsigned short, b1) << 16);
+  const unsigned int hi = (unsigned int)__builtin_bit_cast(unsigned short, b2) |
+                          ((unsigned int)__builtin_bit_cast(unsigned short, b3) << 16);
+  *reinterpret_cast<u32x2_t*>(p) = u32x2_t{lo, hi};
+}
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding:
+// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BN> struct Stages { static constexpr int value = BN > 160 ? 2 : 3; };
+
+template <int BN, int AMODE, int EPI>
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm256_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
+  constexpr int STAGES = Stages<BN>::value;
+  constexpr int WN = BN / 2;                 // columns per wave
+  constexpr int NTW = WN / 16;               // 16-column tiles per wave
+  constexpr int A_UNITS = BM * KU;           // 2048 units per stage
+  constexpr int B_UNITS = BN * KU;
+  constexpr int A_LOADS = A_UNITS / NTHR;    // 8 loads per thread per step
+  constexpr int B_LOADS = (B_UNITS + NTHR - 1) / NTHR;
+  // loads every wave issues per step (a wave may issue one more B load; the
+  // waits below count only the guaranteed ones, which waits a little longer
+  // on those waves and never too little)
+  constexpr int LOADS = A_LOADS + B_UNITS / NTHR;
+  // one LDS object per stage: the compiler gives each its own alias scope, so
+  // waiting for one stage's direct loads does not wait for the others
+  __shared__ u32x4_t As0[A_UNITS], As1[A_UNITS], As2[STAGES > 2 ? A_UNITS : 1];
+  __shared__ u32x4_t Bs0[B_UNITS], Bs1[B_UNITS], Bs2[STAGES > 2 ? B_UNITS : 1];
+
+  const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (tile >= nM * nN) return;
+  const int per_group = GROUP_M * nN;
+  const int group = tile / per_group;
+  const int first_m = group * GROUP_M;
+  const int gsize = min(nM - first_m, GROUP_M);
+  const int in_g = tile - group * per_group;
+  const int m0 = (first_m + in_g % gsize) * BM;
+  const int n0 = (in_g / gsize) * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int M = p.M, N = p.N, K = p.K;
+
+  // ---- per-lane source of each direct load -------------------------------
+  // Load j of this wave fills LDS units [(j * 4 + wave) * 64, +64) of the
+  // stage, i.e. the 8 rows (j * 4 + wave) * 8 + 0..7; LDS unit q holds row
+  // q / 8, logical unit swz(q % 8, row).  So lane l always loads row
+  // (j * 4 + wave) * 8 + l / 8 and logical unit (l % 8) ^ (l / 8): the unit is
+  // the same for every load of a lane and the row advances by 32 per load.
+  const int lrow8 = lane >> 3;
+  const int lunit = (lane & 7) ^ lrow8;
+  const char* a_base;
+  unsigned a_bytes;
+  if (AMODE == A_PLAIN) {
+    a_base = (const char*)p.A + (size_t)m0 * p.lda * 2;
+    a_bytes = (unsigned)((size_t)(M - m0) * p.lda * 2);
+  } else {
+    a_base = (const char*)p.A;
+    a_bytes = (unsigned)p.a_bytes;
+  }
+  // A_PLAIN: offset of load j = a_off0 + j * a_step + 2 k, k = k0 + 8 * lunit.
+  // Rows past M give offsets past a_bytes and load zero.
+  const unsigned a_step = (unsigned)(32 * p.lda * 2);
+  const unsigned a_off0 = (unsigned)((wave * 8 + lrow8) * p.lda * 2);
+  // A_ROWMAP: per-load row offsets; A_CONV: per-load chunk offset and pixel
+  unsigned a_rowoff[AMODE == A_PLAIN ? 1 : A_LOADS];
+  int a_pix[AMODE == A_CONV ? A_LOADS : 1];  // (oy << 16) | ox, or -1 past M
+  if (AMODE != A_PLAIN) {
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j) {
+      const int m = m0 + (j * 4 + wave) * 8 + lrow8;
+      if (AMODE == A_ROWMAP) {
+        a_rowoff[j] = m < M ? (unsigned)((size_t)(p.rowmap[m] - p.rowmap_base) * p.lda * 2) : OOB;
+      } else {
+        a_rowoff[j] = 0;
+        a_pix[j] = -1;
+        if (m < M) {
+          const int hw = p.hout * p.wout;
+          const int chunk = m / hw;
+          const int rem = m - chunk * hw;
+          int oy, ox;
+          if (p.xmajor) {
+            ox = rem / p.hout;
+            oy = rem - ox * p.hout;
+          } else {
+            oy = rem / p.wout;
+            ox = rem - oy * p.wout;
+          }
+          a_pix[j] = (oy << 16) | ox;
+          a_rowoff[j] = (unsigned)((size_t)chunk * p.hin * p.win * p.cin * 2);
+        }
+      }
+    }
+  }
+  // B: offset of load j = b_off0 + j * b_step + 2 k; rows past N load zero.
+  const char* b_base = (const char*)p.B + (size_t)n0 * p.ldb * 2;
+  const unsigned b_bytes = (unsigned)((size_t)(N - n0) * p.ldb * 2);
+  const unsigned b_step = (unsigned)(32 * p.ldb * 2);
+  const unsigned b_off0 = (unsigned)((wave * 8 + lrow8) * p.ldb * 2);
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t b_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_bytes, 0x00020000);
+
+  auto issue = [&](int kt, u32x4_t* As_s, u32x4_t* Bs_s) {
+    const int k = kt * BK + lunit * 8;
+    // k past K: an offset that is past every buffer
+    const unsigned koff = k < K ? (unsigned)(2 * k) : OOB;
+    if (AMODE == A_CONV) {
+      const int tap = k / p.cin;
+      const int ci = k - tap * p.cin;
+      const int kh = tap / 3;
+      const int kw = tap - 3 * kh;
+#pragma unroll
+      for (int j = 0; j < A_LOADS; ++j) {
+        const int oy = a_pix[j] >> 16, ox = a_pix[j] & 0xFFFF;
+        const int iy = 2 * oy + kh - 1;
+        const int ix = 2 * ox + kw - 1;
+        const bool ok = a_pix[j] >= 0 && k < K && iy >= 0 && iy < p.hin && ix >= 0 && ix < p.win;
+        const unsigned off = ok ? a_rowoff[j] + (unsigned)(((iy * p.win + ix) * p.cin + ci) * 2) : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(j * 4 + wave) * 64]), 16,
+                                                 off, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < A_LOADS; ++j) {
+        const unsigned off = AMODE == A_PLAIN ? a_off0 + j * a_step + koff
+                                              : (a_rowoff[j] == OOB ? OOB : a_rowoff[j] + koff);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(j * 4 + wave) * 64]), 16,
+                                                 off, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j) {
+      if ((j * 4 + wave) * 64 < B_UNITS) {  // uniform per wave
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dma_dst(&Bs_s[(j * 4 + wave) * 64]), 16,
+                                                 b_off0 + j * b_step + koff, 0, 0, 0);
+      }
+    }
+  };
+
+  f32x4_t acc[NTW][8];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (K + BK - 1) / BK;
+  const int lrow = lane & 15;
+  const int g = lane >> 4;
+  // one k step from a given stage: wait for this thread's loads of step kt
+  // (the steps issued after it, at most STAGES - 2, may stay in flight),
+  // barrier so that every wave's loads have landed and step kt - 1 is
+  // consumed, refill the stage step kt - 1 used with step kt + STAGES - 1,
+  // then the matrix instructions of the two 32-deep halves of the step
+  auto step = [&](int kt, const u32x4_t* As_s, const u32x4_t* Bs_s, u32x4_t* As_n, u32x4_t* Bs_n) {
+    const int after = min(nk - 1 - kt, STAGES - 2);
+    if (after >= 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, As_n, Bs_n);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      // fragments: all of B and the first two of A up front, then each further
+      // A fragment is read while the matrix instructions of an earlier one run
+      const int u = 4 * s + g;
+      FragBF16 xa[8], wb[NTW];
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int r = wn * WN + 16 * j + lrow;
+        frag_from_units(wb[j], Bs_s[r * KU + swz(u, r)], zero_unit());
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = wm * 128 + 16 * i + lrow;
+        frag_from_units(xa[i], As_s[r * KU + swz(u, r)], zero_unit());
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) mma16_k32(acc[j][i], wb[j], xa[i]);
+      __builtin_amdgcn_sched_group_barrier(0x100, NTW + 2, 0);  // DS reads
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NTW, 0);     // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTW, 0);
+      __builtin_amdgcn_sched_barrier(0);  // keep the halves apart: fewer live fragments
+    }
+  };
+
+  static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
+  if (STAGES == 2) {
+    issue(0, As0, Bs0);
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(kt, As0, Bs0, As1, Bs1);
+      if (kt + 1 < nk) step(kt + 1, As1, Bs1, As0, Bs0);
+    }
+  } else {
+    issue(0, As0, Bs0);
+    if (1 < nk) issue(1, As1, Bs1);
+    for (int kt = 0; kt < nk; kt += 3) {
+      step(kt, As0, Bs0, As2, Bs2);
+      if (kt + 1 < nk) step(kt + 1, As1, Bs1, As0, Bs0);
+      if (kt + 2 < nk) step(kt + 2, As2, Bs2, As1, Bs1);
+    }
+  }
+  wait_vmcnt<0>();
+
+  // epilogue: lane holds C[m0 + wm*128 + 16 i + lrow][n0 + wn*WN + 16 j + 4 g + r]
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int n = n0 + wn * WN + 16 * j + 4 * g;
+    if (n >= N) continue;
+    float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p.bias) bq = *reinterpret_cast<const float4*>(p.bias + n);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + wm * 128 + 16 * i + lrow;
+      if (m >= M) continue;
+      float v[4] = {acc[j][i][0] + bq.x, acc[j][i][1] + bq.y, acc[j][i][2] + bq.z,
+                    acc[j][i][3] + bq.w};
+      const size_t off = (size_t)m * p.ldo + n;
+      if (EPI == EPI_STORE) {
+        store4((bf16_t*)p.out + off, v);
+      } else if (EPI == EPI_STORE_GELU) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = gelu_f(v[r]);
+        store4((bf16_t*)p.out + off, v);
+      } else if (EPI == EPI_RESID) {
+        float4* o = reinterpret_cast<float4*>((float*)p.out + off);
+        float4 x = *o;
+        x.x += v[0]; x.y += v[1]; x.z += v[2]; x.w += v[3];
+        *o = x;
+      } else if (EPI == EPI_PE) {
+        const int jpos = p.rowmap[m] % p.tpc;
+        const float4 q = *reinterpret_cast<const float4*>(p.pe + (size_t)jpos * N + n);
+        *reinterpret_cast<float4*>((float*)p.out + off) =
+            make_float4(v[0] + q.x, v[1] + q.y, v[2] + q.z, v[3] + q.w);
+      } else {
+        *reinterpret_cast<float4*>((float*)p.out + off) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
+
+template <int BN, int AMODE, int EPI>
+hipError_t run(const GemmArgs& a, hipStream_t s) {
+  const int nM = (a.M + BM - 1) / BM;
+  const int nN = (a.N + BN - 1) / BN;
+  const int tiles = nM * nN;
+  const int per_xcd = (tiles + 7) / 8;
+  hipLaunchKernelGGL((gemm256_kernel<BN, AMODE, EPI>), dim3(8 * per_xcd), dim3(NTHR), 0, s, a, nM,
+                     nN, per_xcd);
+  return hipGetLastError();
+}
+
+template <int BN>
+hipError_t dispatch(const GemmArgs& a, int amode, int epi, hipStream_t s) {
+  if (amode == A_PLAIN) {
+    switch (epi) {
+      case EPI_STORE: return run<BN, A_PLAIN, EPI_STORE>(a, s);
+      case EPI_STORE_GELU: return run<BN, A_PLAIN, EPI_STORE_GELU>(a, s);
+      case EPI_RESID: return run<BN, A_PLAIN, EPI_RESID>(a, s);
+      case EPI_STORE_F32: return run<BN, A_PLAIN, EPI_STORE_F32>(a, s);
+      default: break;
+    }
+  } else if (amode == A_CONV && epi == EPI_STORE_GELU) {
+    return run<BN, A_CONV, EPI_STORE_GELU>(a, s);
+  } else if (amode == A_ROWMAP && epi == EPI_PE) {
+    return run<BN, A_ROWMAP, EPI_PE>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Column tile for an N: the candidate that wastes the fewest tile slots on 256
+// CUs (partly empty last wave and columns past N), ties to the wider tile.
+int pick_bn(int M, int N) {
+  const int cands[2] = {160, 128};
+  const int nM = (M + BM - 1) / BM;
+  int best = 160;
+  double best_eff = -1.0;
+  for (int bn : cands) {
+    const int nN = (N + bn - 1) / bn;
+    const long tiles = (long)nM * nN;
+    const long slots = ((tiles + 255) / 256) * 256;
+    const double eff = (double)tiles / (double)slots * (double)N / (double)(nN * bn);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = bn;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+int g_gemm256_force_bn = 0;  // tuning hook: 0 = automatic
+
+hipError_t launch_gemm256(const GemmArgs& a, int amode, int epi, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  const int bn = g_gemm256_force_bn ? g_gemm256_force_bn : pick_bn(a.M, a.N);
+  switch (bn) {
+    case 160: return dispatch<160>(a, amode, epi, s);
+    case 128: return dispatch<128>(a, amode, epi, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm(const GemmArgs& a, int amode, int epi, aut_dtype dt, hipStream_t s) {
+  if (dt == AUT_BF16) return launch_gemm256(a, amode, epi, s);
+  return launch_gemm128(a, amode, epi, dt, s);
+}
+
+}  // namespace aut
