@@ -10,10 +10,31 @@ typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 
 typedef __bf16 bf16_t;
 
-// Exact GELU, x * Phi(x), with the device library's erff ('gelu' activation of
-// AuTEncoderConfig; the erf form, not the tanh approximation).
+// GELU, x * Phi(x) with Phi(x) = erfc(-x / sqrt 2) / 2 ('gelu' activation of
+// AuTEncoderConfig: the erf form, not the tanh approximation).
+//
+// erfc(z), z >= 0, by the Chebyshev fit of Numerical Recipes (Press et al.,
+// section 6.2, "erfcc"): erfc(z) = t exp(-z^2 + P(t)), t = 1 / (1 + z / 2),
+// P of degree 9, fractional error below 1.2e-7 for every z >= 0; negative
+// arguments use erfc(-z) = 2 - erfc(z).  Branch-free: one reciprocal, one
+// exp2 and ten fused multiply-adds, so a wavefront never splits over it.
 __device__ __forceinline__ float gelu_f(float x) {
-  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
+  const float z = fabsf(x) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
+  float p = 0.17087277f;
+  p = fmaf(p, t, -0.82215223f);
+  p = fmaf(p, t, 1.48851587f);
+  p = fmaf(p, t, -1.13520398f);
+  p = fmaf(p, t, 0.27886807f);
+  p = fmaf(p, t, -0.18628806f);
+  p = fmaf(p, t, 0.09678418f);
+  p = fmaf(p, t, 0.37409196f);
+  p = fmaf(p, t, 1.00002368f);
+  p = fmaf(p, t, -1.26551223f);
+  const float e = fmaf(-z, z, p);                       // natural-log exponent
+  const float half_erfc = 0.5f * t * __builtin_amdgcn_exp2f(e * 1.44269504088896341f);
+  const float phi = x >= 0.f ? 1.0f - half_erfc : half_erfc;
+  return x * phi;
 }
 
 // fp32 -> bf16, round to nearest even (hardware conversion on gfx950).

@@ -1,12 +1,15 @@
 // Conv-stem first layer, parameter packing and the sinusoid position table.
 //
 // conv1 has one input channel and 9 taps per output, far too little depth for
-// the matrix cores, so it runs on the vector ALU in fp32: a workgroup makes
-// one output row (oy) of one chunk, with the three input mel rows it needs
-// staged in LDS and zero-filled past the chunk's valid frames (the m-star
+// the matrix cores, so it runs on the vector ALU in fp32.  A workgroup makes
+// CONV1_ROWS output rows of one chunk: the 2 CONV1_ROWS + 1 input mel rows it
+// needs are staged in LDS, zero past the chunk's valid frames (the m-star
 // frontend zero-pads the last piece of a request to a full chunk) and outside
-// the image (padding 1).  Output: channels-last [chunk][y][x][c], the operand
-// layout of the conv2 implicit GEMM.
+// the image (padding 1).  Each thread owns 8 consecutive output channels, keeps
+// their 72 weights and 8 biases in registers, and walks output pixels: per
+// pixel 9 broadcast LDS reads, 72 FMAs, 8 GELUs and one 16-byte store of the
+// 8 bf16 results.  Output: channels-last [chunk][y][x][c], the operand layout
+// of the conv2 implicit GEMM.
 #include <math.h>
 
 #include "aut_internal.h"
@@ -17,52 +20,78 @@ namespace aut {
 namespace {
 
 constexpr int CONV1_THREADS = 256;
-constexpr int MAX_C = 1024;
+constexpr int CONV1_ROWS = 4;   // output rows per workgroup
 constexpr int MAX_CF = 256;
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&v)[8]);
+template <>
+__device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float (&v)[8]) {
+  bf16x8_t b = {to_bf16(v[0]), to_bf16(v[1]), to_bf16(v[2]), to_bf16(v[3]),
+                to_bf16(v[4]), to_bf16(v[5]), to_bf16(v[6]), to_bf16(v[7])};
+  *reinterpret_cast<bf16x8_t*>(p) = b;
+}
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float (&v)[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
 
 template <typename T>
 __global__ __launch_bounds__(CONV1_THREADS) void conv1_kernel(
     const float* __restrict__ feat, int T_max, int mel, const int* __restrict__ chunks,
     int chunk_first, const float* __restrict__ w1, const float* __restrict__ b1,
     T* __restrict__ a1, int C, int cf, int h1, int w1out) {
-  __shared__ float img[3][MAX_CF + 2];
-  __shared__ float ws[MAX_C * 9];
-  __shared__ float bs[MAX_C];
-  const int oy = blockIdx.x;
+  __shared__ float img[2 * CONV1_ROWS + 1][MAX_CF + 2];
+  const int oy0 = blockIdx.x * CONV1_ROWS;
   const int cl = blockIdx.y;  // chunk within the batch
   const int* ch = chunks + 5 * (chunk_first + cl);
   const int req = ch[0], frame0 = ch[1], vf = ch[2];
   const int tid = threadIdx.x;
 
-  for (int idx = tid; idx < 3 * (cf + 2); idx += CONV1_THREADS) {
-    const int kh = idx / (cf + 2);
-    const int ix = idx - kh * (cf + 2) - 1;  // -1 .. cf
-    const int iy = 2 * oy + kh - 1;
+  // input rows 2 oy0 - 1 .. 2 (oy0 + CONV1_ROWS) - 1, columns -1 .. cf
+  for (int idx = tid; idx < (2 * CONV1_ROWS + 1) * (cf + 2); idx += CONV1_THREADS) {
+    const int r = idx / (cf + 2);
+    const int ix = idx - r * (cf + 2) - 1;
+    const int iy = 2 * oy0 - 1 + r;
     float v = 0.f;
     if (iy >= 0 && iy < mel && ix >= 0 && ix < vf)
       v = feat[((size_t)req * mel + iy) * T_max + frame0 + ix];
-    img[kh][ix + 1] = v;
+    img[r][ix + 1] = v;
   }
-  for (int idx = tid; idx < 9 * C; idx += CONV1_THREADS) ws[idx] = w1[idx];
-  for (int idx = tid; idx < C; idx += CONV1_THREADS) bs[idx] = b1[idx];
   __syncthreads();
 
-  T* out = a1 + ((size_t)cl * h1 + oy) * w1out * C;
-  const int half = C >> 1;
-  for (int idx = tid; idx < w1out * half; idx += CONV1_THREADS) {
-    const int ox = idx / half;
-    const int c = 2 * (idx - ox * half);
-    float v0 = bs[c], v1 = bs[c + 1];
+  const int groups = C >> 3;                     // 8-channel groups
+  const int xlanes = CONV1_THREADS / groups;     // threads per group
+  const int cg = tid % groups;
+  const int xl = tid / groups;
+  if (xl >= xlanes) return;                      // spare threads (no barrier follows)
+  const int c0 = cg * 8;
+  float w[8][9], bias[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    bias[k] = b1[c0 + k];
+#pragma unroll
+    for (int t = 0; t < 9; ++t) w[k][t] = w1[(c0 + k) * 9 + t];
+  }
+  const int rows = min(CONV1_ROWS, h1 - oy0);
+  for (int item = xl; item < rows * w1out; item += xlanes) {
+    const int ry = item / w1out;
+    const int ox = item - ry * w1out;
+    float x[9];
 #pragma unroll
     for (int kh = 0; kh < 3; ++kh)
 #pragma unroll
-      for (int kw = 0; kw < 3; ++kw) {
-        const float x = img[kh][2 * ox + kw];  // column 2 ox + kw - 1, shifted by the pad
-        v0 = fmaf(ws[c * 9 + kh * 3 + kw], x, v0);
-        v1 = fmaf(ws[(c + 1) * 9 + kh * 3 + kw], x, v1);
-      }
-    out[(size_t)ox * C + c] = from_f32<T>(gelu_f(v0));
-    out[(size_t)ox * C + c + 1] = from_f32<T>(gelu_f(v1));
+      for (int kw = 0; kw < 3; ++kw) x[kh * 3 + kw] = img[2 * ry + kh][2 * ox + kw];
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float a = bias[k];
+#pragma unroll
+      for (int t = 0; t < 9; ++t) a = fmaf(w[k][t], x[t], a);
+      v[k] = gelu_f(a);
+    }
+    store8<T>(a1 + (((size_t)cl * h1 + oy0 + ry) * w1out + ox) * C + c0, v);
   }
 }
 
@@ -116,8 +145,8 @@ hipError_t launch_conv1(const float* feat, int T_max, const int* chunks, int chu
                         const float* w1, const float* b1, void* a1, aut_dtype dt,
                         const Geometry& g, hipStream_t s) {
   if (nb <= 0) return hipSuccess;
-  if (g.C > MAX_C || g.cf > MAX_CF || (g.C & 1)) return hipErrorInvalidValue;
-  dim3 grid(g.h1, nb);
+  if (g.cf > MAX_CF || (g.C & 7) || (g.C >> 3) > CONV1_THREADS) return hipErrorInvalidValue;
+  dim3 grid((g.h1 + CONV1_ROWS - 1) / CONV1_ROWS, nb);
   if (dt == AUT_BF16)
     hipLaunchKernelGGL(conv1_kernel<bf16_t>, grid, dim3(CONV1_THREADS), 0, s, feat, T_max, g.mel,
                        chunks, chunk_first, w1, b1, (bf16_t*)a1, g.C, g.cf, g.h1, g.w1);
