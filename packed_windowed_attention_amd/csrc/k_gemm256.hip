@@ -319,6 +319,232 @@ void gemm256_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   }
 }
 
+// Eight-wave variant for wide column tiles (BN = 256 or 320): 8 waves (2 per
+// SIMD) in a 2 x 4 grid, each wave 128 x BN/4 (128 or 160 accumulators), two
+// LDS stages of 64 or 72 KiB.  Fewer operand bytes per flop than the
+// four-wave kernel: the memory path, not the matrix cores, bounds these GEMMs
+// (about one 128-byte request per 10 cycles per CU at ~420 cycles of L2
+// latency), and a 256 x 320 tile needs 7.0 bytes per k step per 1000 flops
+// against 10.2 for 256 x 160.
+template <int BN, int AMODE, int EPI>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
+  constexpr int NT8 = 512;
+  constexpr int WN = BN / 4;                 // columns per wave
+  constexpr int NTW = WN / 16;               // 16-column tiles per wave
+  constexpr int A_UNITS = BM * KU;           // 2048 units per stage
+  constexpr int B_UNITS = BN * KU;
+  constexpr int A_LOADS = A_UNITS / NT8;     // 4 loads per thread per step
+  constexpr int B_LOADS = B_UNITS / NT8;     // 4 or 5
+  static_assert(B_UNITS % NT8 == 0, "whole B loads per thread");
+  __shared__ u32x4_t As0[A_UNITS], As1[A_UNITS];
+  __shared__ u32x4_t Bs0[B_UNITS], Bs1[B_UNITS];
+
+  const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (tile >= nM * nN) return;
+  const int per_group = GROUP_M * nN;
+  const int group = tile / per_group;
+  const int first_m = group * GROUP_M;
+  const int gsize = min(nM - first_m, GROUP_M);
+  const int in_g = tile - group * per_group;
+  const int m0 = (first_m + in_g % gsize) * BM;
+  const int n0 = (in_g / gsize) * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+  const int wm = wave >> 2, wn = wave & 3;
+  const int M = p.M, N = p.N, K = p.K;
+
+  // load j of this wave fills LDS units [(j * 8 + wave) * 64, +64): rows
+  // (j * 8 + wave) * 8 + 0..7, unit (l % 8) ^ (l / 8) for lane l
+  const int lrow8 = lane >> 3;
+  const int lunit = (lane & 7) ^ lrow8;
+  const char* a_base;
+  unsigned a_bytes;
+  if (AMODE == A_PLAIN) {
+    a_base = (const char*)p.A + (size_t)m0 * p.lda * 2;
+    a_bytes = (unsigned)((size_t)(M - m0) * p.lda * 2);
+  } else {
+    a_base = (const char*)p.A;
+    a_bytes = (unsigned)p.a_bytes;
+  }
+  const unsigned a_step = (unsigned)(64 * p.lda * 2);
+  const unsigned a_off0 = (unsigned)((wave * 8 + lrow8) * p.lda * 2);
+  unsigned a_rowoff[AMODE == A_PLAIN ? 1 : A_LOADS];
+  int a_pix[AMODE == A_CONV ? A_LOADS : 1];
+  if (AMODE != A_PLAIN) {
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j) {
+      const int m = m0 + (j * 8 + wave) * 8 + lrow8;
+      if (AMODE == A_ROWMAP) {
+        a_rowoff[j] = m < M ? (unsigned)((size_t)(p.rowmap[m] - p.rowmap_base) * p.lda * 2) : OOB;
+      } else {
+        a_rowoff[j] = 0;
+        a_pix[j] = -1;
+        if (m < M) {
+          const int hw = p.hout * p.wout;
+          const int chunk = m / hw;
+          const int rem = m - chunk * hw;
+          int oy, ox;
+          if (p.xmajor) {
+            ox = rem / p.hout;
+            oy = rem - ox * p.hout;
+          } else {
+            oy = rem / p.wout;
+            ox = rem - oy * p.wout;
+          }
+          a_pix[j] = (oy << 16) | ox;
+          a_rowoff[j] = (unsigned)((size_t)chunk * p.hin * p.win * p.cin * 2);
+        }
+      }
+    }
+  }
+  const char* b_base = (const char*)p.B + (size_t)n0 * p.ldb * 2;
+  const unsigned b_bytes = (unsigned)((size_t)(N - n0) * p.ldb * 2);
+  const unsigned b_step = (unsigned)(64 * p.ldb * 2);
+  const unsigned b_off0 = (unsigned)((wave * 8 + lrow8) * p.ldb * 2);
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t b_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_bytes, 0x00020000);
+
+  auto issue = [&](int kt, u32x4_t* As_s, u32x4_t* Bs_s) __attribute__((always_inline)) {
+    const int k = kt * BK + lunit * 8;
+    const unsigned koff = k < K ? (unsigned)(2 * k) : OOB;
+    if (AMODE == A_CONV) {
+      const int tap = k / p.cin;
+      const int ci = k - tap * p.cin;
+      const int kh = tap / 3;
+      const int kw = tap - 3 * kh;
+#pragma unroll
+      for (int j = 0; j < A_LOADS; ++j) {
+        const int oy = a_pix[j] >> 16, ox = a_pix[j] & 0xFFFF;
+        const int iy = 2 * oy + kh - 1;
+        const int ix = 2 * ox + kw - 1;
+        const bool ok = a_pix[j] >= 0 && k < K && iy >= 0 && iy < p.hin && ix >= 0 && ix < p.win;
+        const unsigned off = ok ? a_rowoff[j] + (unsigned)(((iy * p.win + ix) * p.cin + ci) * 2) : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(j * 8 + wave) * 64]), 16,
+                                                 off, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < A_LOADS; ++j) {
+        const unsigned off = AMODE == A_PLAIN ? a_off0 + j * a_step + koff
+                                              : (a_rowoff[j] == OOB ? OOB : a_rowoff[j] + koff);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(j * 8 + wave) * 64]), 16,
+                                                 off, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dma_dst(&Bs_s[(j * 8 + wave) * 64]), 16,
+                                               b_off0 + j * b_step + koff, 0, 0, 0);
+  };
+
+  f32x4_t acc[NTW][8];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (K + BK - 1) / BK;
+  const int lrow = lane & 15;
+  const int g = lane >> 4;
+  // one step from a stage: wait for this thread's loads of step kt (nothing
+  // later is in flight yet), barrier so that every wave's loads have landed
+  // and step kt - 1 is consumed, load step kt + 1 into the other stage, then
+  // the matrix instructions of the two 32-deep halves of the step
+  auto step = [&](int kt, const u32x4_t* As_s, const u32x4_t* Bs_s, u32x4_t* As_n, u32x4_t* Bs_n)
+      __attribute__((always_inline)) {
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 1 < nk) issue(kt + 1, As_n, Bs_n);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int u = 4 * h + g;
+      FragBF16 xa[8], wb[NTW];
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int r = wn * WN + 16 * j + lrow;
+        frag_from_units(wb[j], Bs_s[r * KU + swz(u, r)], zero_unit());
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = wm * 128 + 16 * i + lrow;
+        frag_from_units(xa[i], As_s[r * KU + swz(u, r)], zero_unit());
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) mma16_k32(acc[j][i], wb[j], xa[i]);
+      __builtin_amdgcn_sched_group_barrier(0x100, NTW + 2, 0);  // DS reads
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NTW, 0);     // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTW, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  issue(0, As0, Bs0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, As0, Bs0, As1, Bs1);
+    if (kt + 1 < nk) step(kt + 1, As1, Bs1, As0, Bs0);
+  }
+
+  // epilogue: lane holds C[m0 + wm*128 + 16 i + lrow][n0 + wn*WN + 16 j + 4 g + r]
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int n = n0 + wn * WN + 16 * j + 4 * g;
+    if (n >= N) continue;
+    float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p.bias) bq = *reinterpret_cast<const float4*>(p.bias + n);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + wm * 128 + 16 * i + lrow;
+      if (m >= M) continue;
+      float v[4] = {acc[j][i][0] + bq.x, acc[j][i][1] + bq.y, acc[j][i][2] + bq.z,
+                    acc[j][i][3] + bq.w};
+      const size_t off = (size_t)m * p.ldo + n;
+      if (EPI == EPI_STORE) {
+        store4((bf16_t*)p.out + off, v);
+      } else if (EPI == EPI_STORE_GELU) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = gelu_f(v[r]);
+        store4((bf16_t*)p.out + off, v);
+      } else if (EPI == EPI_RESID) {
+        float4* o = reinterpret_cast<float4*>((float*)p.out + off);
+        float4 x = *o;
+        x.x += v[0]; x.y += v[1]; x.z += v[2]; x.w += v[3];
+        *o = x;
+      } else if (EPI == EPI_PE) {
+        const int jpos = p.rowmap[m] % p.tpc;
+        const float4 q = *reinterpret_cast<const float4*>(p.pe + (size_t)jpos * N + n);
+        *reinterpret_cast<float4*>((float*)p.out + off) =
+            make_float4(v[0] + q.x, v[1] + q.y, v[2] + q.z, v[3] + q.w);
+      } else {
+        *reinterpret_cast<float4*>((float*)p.out + off) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
+
+template <int BN, int AMODE, int EPI>
+hipError_t run8(const GemmArgs& a, hipStream_t s) {
+  const int nM = (a.M + BM - 1) / BM;
+  const int nN = (a.N + BN - 1) / BN;
+  const int tiles = nM * nN;
+  const int per_xcd = (tiles + 7) / 8;
+  hipLaunchKernelGGL((gemm8w_kernel<BN, AMODE, EPI>), dim3(8 * per_xcd), dim3(512), 0, s, a, nM,
+                     nN, per_xcd);
+  return hipGetLastError();
+}
+
 template <int BN, int AMODE, int EPI>
 hipError_t run(const GemmArgs& a, hipStream_t s) {
   const int nM = (a.M + BM - 1) / BM;
@@ -330,36 +556,47 @@ hipError_t run(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BN, int AMODE, int EPI>
+hipError_t run_any(const GemmArgs& a, hipStream_t s) {
+  if constexpr (BN >= 256) return run8<BN, AMODE, EPI>(a, s);
+  else return run<BN, AMODE, EPI>(a, s);
+}
+
 template <int BN>
 hipError_t dispatch(const GemmArgs& a, int amode, int epi, hipStream_t s) {
   if (amode == A_PLAIN) {
     switch (epi) {
-      case EPI_STORE: return run<BN, A_PLAIN, EPI_STORE>(a, s);
-      case EPI_STORE_GELU: return run<BN, A_PLAIN, EPI_STORE_GELU>(a, s);
-      case EPI_RESID: return run<BN, A_PLAIN, EPI_RESID>(a, s);
-      case EPI_STORE_F32: return run<BN, A_PLAIN, EPI_STORE_F32>(a, s);
+      case EPI_STORE: return run_any<BN, A_PLAIN, EPI_STORE>(a, s);
+      case EPI_STORE_GELU: return run_any<BN, A_PLAIN, EPI_STORE_GELU>(a, s);
+      case EPI_RESID: return run_any<BN, A_PLAIN, EPI_RESID>(a, s);
+      case EPI_STORE_F32: return run_any<BN, A_PLAIN, EPI_STORE_F32>(a, s);
       default: break;
     }
   } else if (amode == A_CONV && epi == EPI_STORE_GELU) {
-    return run<BN, A_CONV, EPI_STORE_GELU>(a, s);
+    return run_any<BN, A_CONV, EPI_STORE_GELU>(a, s);
   } else if (amode == A_ROWMAP && epi == EPI_PE) {
-    return run<BN, A_ROWMAP, EPI_PE>(a, s);
+    return run_any<BN, A_ROWMAP, EPI_PE>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
-// Column tile for an N: the candidate that wastes the fewest tile slots on 256
-// CUs (partly empty last wave and columns past N), ties to the wider tile.
+// Column tile for an N: the candidate with the best estimated throughput,
+// i.e. tile-slot use on 256 CUs (partly empty last round, columns past N)
+// times the measured relative speed of the kernel (the eight-wave kernels for
+// BN = 320 and 256 move about 25% fewer bytes per flop and run that much
+// faster per tile); ties to the first candidate.
 int pick_bn(int M, int N) {
-  const int cands[2] = {160, 128};
+  const int cands[4] = {320, 256, 160, 128};
+  const double speed[4] = {1.25, 1.25, 1.0, 1.0};
   const int nM = (M + BM - 1) / BM;
-  int best = 160;
+  int best = 320;
   double best_eff = -1.0;
-  for (int bn : cands) {
+  for (int c = 0; c < 4; ++c) {
+    const int bn = cands[c];
     const int nN = (N + bn - 1) / bn;
     const long tiles = (long)nM * nN;
     const long slots = ((tiles + 255) / 256) * 256;
-    const double eff = (double)tiles / (double)slots * (double)N / (double)(nN * bn);
+    const double eff = speed[c] * (double)tiles / (double)slots * (double)N / (double)(nN * bn);
     if (eff > best_eff + 1e-9) {
       best_eff = eff;
       best = bn;
@@ -376,6 +613,8 @@ hipError_t launch_gemm256(const GemmArgs& a, int amode, int epi, hipStream_t s) 
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   const int bn = g_gemm256_force_bn ? g_gemm256_force_bn : pick_bn(a.M, a.N);
   switch (bn) {
+    case 320: return dispatch<320>(a, amode, epi, s);
+    case 256: return dispatch<256>(a, amode, epi, s);
     case 160: return dispatch<160>(a, amode, epi, s);
     case 128: return dispatch<128>(a, amode, epi, s);
     default: return hipErrorInvalidValue;
