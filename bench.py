@@ -28,6 +28,15 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix/vector peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# HBM traffic of the layer GEMMs, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+# scaled by a copy of known size; valid only for the kernel sources it was
+# taken with (their SHA-256 is stored beside the figures).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_wide_hbm_traffic.md")
+GEMM_SOURCES = ("packed_windowed_attention_amd/csrc/k_gemm256.hip",
+                "packed_windowed_attention_amd/csrc/device_common.h",
+                "packed_windowed_attention_amd/csrc/aut_internal.h")
+LAYER_GEMM_RE = r"gemm(8w|256)_kernel<\d+, 0, \d+>"
+
 METRIC = "encoder tokens/s and audio-sec/s on 1 MI355X; % of bf16 MFMA peak"
 
 DESCR = {
@@ -42,6 +51,80 @@ DESCR = {
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemm_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload):
+    """Bytes per layer-GEMM launch from the stored counter summary, or None
+    when it is missing, for another workload, or for other kernel sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(blob)
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("source_sha256") != gemm_source_sha():
+        return None
+    return rec["bytes_per_launch"]
+
+
+def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_mib, cmds):
+    """Writes the HBM-traffic summary of the layer GEMMs from rocprofv3 counter
+    CSVs: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of one bench step, each
+    scaled by bytes / counter of a device copy of cal_mib MiB."""
+    import csv
+    import re
+
+    def rows(path):
+        with open(path) as f:
+            return list(csv.DictReader(f))
+
+    def factor(path):
+        vals = [float(r["Counter_Value"]) for r in rows(path) if "copyBuffer" in r["Kernel_Name"]]
+        vals = [v for v in vals if v > 0.5 * max(vals)]
+        return cal_mib * 1024.0 / (sum(vals) / len(vals))
+
+    ff, fw = factor(cal_fetch_csv), factor(cal_write_csv)
+    fr, wr = rows(fetch_csv), rows(write_csv)
+    assert len(fr) == len(wr)
+    per = {}
+    for a, b in zip(fr, wr):
+        assert a["Kernel_Name"] == b["Kernel_Name"]
+        name = a["Kernel_Name"]
+        m = re.search(LAYER_GEMM_RE, name)
+        if not m:
+            continue
+        key = m.group(0)
+        e = per.setdefault(key, [0, 0.0, 0.0])
+        e[0] += 1
+        e[1] += float(a["Counter_Value"]) * 1024.0 * ff
+        e[2] += float(b["Counter_Value"]) * 1024.0 * fw
+    n = sum(e[0] for e in per.values())
+    tot = sum(e[1] + e[2] for e in per.values())
+    rec = {"workload": "wide", "kernel": "layer GEMMs (qkv, out_proj, fc1, fc2, proj1, proj2)",
+           "launches": n, "bytes_per_launch": tot / n,
+           "fetch_factor": ff, "write_factor": fw, "source_sha256": gemm_source_sha()}
+    out = ["# HBM traffic of the layer GEMMs: wide workload, bf16, one forward step", "",
+           "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 runs, each",
+           f"scaled by what the same counter reads for a {cal_mib} MiB device-to-device copy",
+           f"(bytes / counter: fetch {ff:.3f}, write {fw:.3f}).", "", "Commands (from /tmp, TMPDIR=/tmp):", "", "```"]
+    out += cmds + ["```", "",
+                   "| kernel | launches | fetch MB / launch | write MB / launch |", "|---|---|---|---|"]
+    for k, (c, f, w) in sorted(per.items()):
+        out.append(f"| `{k}` | {c} | {f / c / 1e6:.1f} | {w / c / 1e6:.1f} |")
+    out += ["", f"All layer GEMMs: {n} launches, {tot / n / 1e6:.1f} MB per launch.", "",
+            "```json", json.dumps(rec, indent=1), "```", ""]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(out))
 
 
 def cpu_baseline(name, cfg_d, lens, feats, P, n_windows):
@@ -82,7 +165,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without per-launch HIP events (no roofline)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 10 device-to-device copies of MIB MiB (the known-size kernel "
+                         "that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                    help="write the layer-GEMM HBM traffic summary from rocprofv3 counter CSVs and exit")
+    ap.add_argument("--calibrate-mib", type=int, default=512)
     args = ap.parse_args()
+    if args.traffic_summary:
+        cmds = [f"rocprofv3 --pmc {c} -f csv -d <out> -o wide -- python <repo>/bench.py --steps 1 --warmup 0 "
+                "--no-cpu-baseline --no-kernel-events" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        cmds += [f"rocprofv3 --pmc {c} -f csv -d <out> -o copy -- python <repo>/bench.py --calibrate-copy "
+                 f"{args.calibrate_mib}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        cmds += ["python <repo>/bench.py --traffic-summary <fetch csv> <write csv> <copy fetch csv> <copy write csv>"]
+        traffic_summary(*args.traffic_summary, args.calibrate_mib, cmds)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the forward pass has no cross-GPU step here "
@@ -96,6 +193,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.calibrate_copy} MiB x 10")
+        return
     name = args.workload
     log(f"generating workload {name}")
     cfg_d, lens, feats, P = si.workload(name)
@@ -188,8 +294,9 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": g["flops"] / g_sec / 1e12 / peak,
-            "traffic": None,
+            "traffic": stored_traffic(name),
             "flops_per_launch": g["flops"] / g["launches"],
+            "algorithmic_bytes_per_launch": g["bytes"] / g["launches"],
             "avg_launch_us": 1e6 * g_sec / g["launches"],
         }
         mf = [stats[c] for c in ("gemm", "attention")]
