@@ -76,6 +76,119 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt lgkmcnt(0) alone, then a workgroup barrier: orders the LDS traffic
+// of the epilogue without waiting for the global stores in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Epilogue through LDS.  A lane's accumulators cover 4 consecutive columns of
+// scattered rows, so storing them straight to memory writes 8- or 16-byte
+// pieces of many cache lines, which the memory system then writes back as
+// partial lines.  Instead the tile goes through LDS (the operand stages are
+// free once the k loop is over) in passes of PR rows: the waves owning those
+// rows write them (bias and GELU applied), then every thread copies 16-byte
+// chunks of whole rows to memory, consecutive threads on consecutive chunks,
+// applying the residual or position add on the way.  The staged rows are
+// spread over the four largest stage arrays, RB rows each, with a row pitch
+// 16 bytes over the row's size so that the 16 rows a wave writes at once fall
+// in distinct banks.  Needs N a multiple of the chunk's element count
+// (checked on the host).
+template <int BN, int WN, int NT, int EPI>
+__device__ __forceinline__ void staged_epilogue(const GemmArgs& p, int m0, int n0, int wm, int wn,
+                                                int tid, f32x4_t (&acc)[WN / 16][8],
+                                                u32x4_t* lds0, u32x4_t* lds1, u32x4_t* lds2,
+                                                u32x4_t* lds3) {
+  constexpr int NTW = WN / 16;
+  constexpr bool F32 = EPI == EPI_RESID || EPI == EPI_PE || EPI == EPI_STORE_F32;
+  constexpr int ES = F32 ? 4 : 2;          // output element size
+  constexpr int PR = F32 ? 64 : 128;       // rows per pass
+  constexpr int RB = PR / 4;               // rows per LDS buffer
+  constexpr int PITCH = BN * ES + 16;      // staged row pitch, bytes
+  constexpr int CPR = BN * ES / 16;        // 16-byte chunks per row
+  constexpr int EPC = 16 / ES;             // elements per chunk
+  constexpr int PER_THREAD = PR * CPR / NT;
+  static_assert(PR * CPR % NT == 0, "whole chunks per thread");
+  const int M = p.M, N = p.N;
+  const int lane = tid & 63, lrow = lane & 15, g = lane >> 4;
+  float4 bq[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int n = n0 + wn * WN + 16 * j + 4 * g;
+    bq[j] = (p.bias && n < N) ? *reinterpret_cast<const float4*>(p.bias + n)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int pass = 0; pass < 256 / PR; ++pass) {
+    lds_barrier();  // the k loop, or the previous pass's copy-out, is done with LDS
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rowt = wm * 128 + 16 * i;  // first tile row of this 16-row block
+      if (rowt / PR != pass) continue;     // uniform over the wave
+      const int lr0 = rowt - pass * PR;
+      const int bsel = lr0 / RB;
+      char* base = (char*)(bsel == 0 ? lds0 : bsel == 1 ? lds1 : bsel == 2 ? lds2 : lds3) +
+                   (lr0 % RB + lrow) * PITCH;
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        f32x4_t av = acc[j][i];
+        asm volatile("" : "+v"(av));  // copy out of the accumulators one tile at a time
+        float v[4] = {av[0] + bq[j].x, av[1] + bq[j].y, av[2] + bq[j].z, av[3] + bq[j].w};
+        if (EPI == EPI_STORE_GELU) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = gelu_f(v[r]);
+        }
+        const int col = wn * WN + 16 * j + 4 * g;
+        if (F32) {
+          *reinterpret_cast<f32x4_t*>(base + col * 4) = f32x4_t{v[0], v[1], v[2], v[3]};
+        } else {
+          const bf16_t b0 = to_bf16(v[0]), b1 = to_bf16(v[1]), b2 = to_bf16(v[2]), b3 = to_bf16(v[3]);
+          *reinterpret_cast<u32x2_t*>(base + col * 2) =
+              u32x2_t{(unsigned)__builtin_bit_cast(unsigned short, b0) |
+                          ((unsigned)__builtin_bit_cast(unsigned short, b1) << 16),
+                      (unsigned)__builtin_bit_cast(unsigned short, b2) |
+                          ((unsigned)__builtin_bit_cast(unsigned short, b3) << 16)};
+        }
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int s = 0; s < PER_THREAD; ++s) {
+      const int q = tid + NT * s;
+      const int r = q / CPR;
+      const int c = q - r * CPR;
+      const int m = m0 + pass * PR + r;
+      const int n = n0 + c * EPC;
+      if (m >= M || n >= N) continue;
+      const int b = r / RB;
+      const char* src = (const char*)(b == 0 ? lds0 : b == 1 ? lds1 : b == 2 ? lds2 : lds3) +
+                        (r - b * RB) * PITCH + c * 16;
+      const u32x4_t d = *reinterpret_cast<const u32x4_t*>(src);
+      const size_t off = (size_t)m * p.ldo + n;
+      if (!F32) {
+        *reinterpret_cast<u32x4_t*>((bf16_t*)p.out + off) = d;
+      } else {
+        // (bit-cast the whole vector: a bit cast of one vector element reads element 0)
+        const f32x4_t f = __builtin_bit_cast(f32x4_t, d);
+        float4 v = make_float4(f[0], f[1], f[2], f[3]);
+        float4* o = reinterpret_cast<float4*>((float*)p.out + off);
+        if (EPI == EPI_RESID) {
+          const float4 x = *o;
+          v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
+        } else if (EPI == EPI_PE) {
+          const int jpos = p.rowmap[m] % p.tpc;
+          const float4 q4 = *reinterpret_cast<const float4*>(p.pe + (size_t)jpos * N + n);
+          v.x += q4.x; v.y += q4.y; v.z += q4.z; v.w += q4.w;
+        }
+        *o = v;
+      }
+    }
+  }
+}
+
 template <int BN> struct Stages { static constexpr int value = BN > 160 ? 2 : 3; };
 
 template <int BN, int AMODE, int EPI>
@@ -282,41 +395,7 @@ void gemm256_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   }
   wait_vmcnt<0>();
 
-  // epilogue: lane holds C[m0 + wm*128 + 16 i + lrow][n0 + wn*WN + 16 j + 4 g + r]
-#pragma unroll
-  for (int j = 0; j < NTW; ++j) {
-    const int n = n0 + wn * WN + 16 * j + 4 * g;
-    if (n >= N) continue;
-    float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (p.bias) bq = *reinterpret_cast<const float4*>(p.bias + n);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = m0 + wm * 128 + 16 * i + lrow;
-      if (m >= M) continue;
-      float v[4] = {acc[j][i][0] + bq.x, acc[j][i][1] + bq.y, acc[j][i][2] + bq.z,
-                    acc[j][i][3] + bq.w};
-      const size_t off = (size_t)m * p.ldo + n;
-      if (EPI == EPI_STORE) {
-        store4((bf16_t*)p.out + off, v);
-      } else if (EPI == EPI_STORE_GELU) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = gelu_f(v[r]);
-        store4((bf16_t*)p.out + off, v);
-      } else if (EPI == EPI_RESID) {
-        float4* o = reinterpret_cast<float4*>((float*)p.out + off);
-        float4 x = *o;
-        x.x += v[0]; x.y += v[1]; x.z += v[2]; x.w += v[3];
-        *o = x;
-      } else if (EPI == EPI_PE) {
-        const int jpos = p.rowmap[m] % p.tpc;
-        const float4 q = *reinterpret_cast<const float4*>(p.pe + (size_t)jpos * N + n);
-        *reinterpret_cast<float4*>((float*)p.out + off) =
-            make_float4(v[0] + q.x, v[1] + q.y, v[2] + q.z, v[3] + q.w);
-      } else {
-        *reinterpret_cast<float4*>((float*)p.out + off) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-    }
-  }
+  staged_epilogue<BN, WN, NTHR, EPI>(p, m0, n0, wm, wn, tid, acc, As0, As1, Bs0, Bs1);
 }
 
 // Eight-wave variant for wide column tiles (BN = 256 or 320): 8 waves (2 per
@@ -497,41 +576,7 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
     if (kt + 1 < nk) step(kt + 1, As1, Bs1, As0, Bs0);
   }
 
-  // epilogue: lane holds C[m0 + wm*128 + 16 i + lrow][n0 + wn*WN + 16 j + 4 g + r]
-#pragma unroll
-  for (int j = 0; j < NTW; ++j) {
-    const int n = n0 + wn * WN + 16 * j + 4 * g;
-    if (n >= N) continue;
-    float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (p.bias) bq = *reinterpret_cast<const float4*>(p.bias + n);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = m0 + wm * 128 + 16 * i + lrow;
-      if (m >= M) continue;
-      float v[4] = {acc[j][i][0] + bq.x, acc[j][i][1] + bq.y, acc[j][i][2] + bq.z,
-                    acc[j][i][3] + bq.w};
-      const size_t off = (size_t)m * p.ldo + n;
-      if (EPI == EPI_STORE) {
-        store4((bf16_t*)p.out + off, v);
-      } else if (EPI == EPI_STORE_GELU) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = gelu_f(v[r]);
-        store4((bf16_t*)p.out + off, v);
-      } else if (EPI == EPI_RESID) {
-        float4* o = reinterpret_cast<float4*>((float*)p.out + off);
-        float4 x = *o;
-        x.x += v[0]; x.y += v[1]; x.z += v[2]; x.w += v[3];
-        *o = x;
-      } else if (EPI == EPI_PE) {
-        const int jpos = p.rowmap[m] % p.tpc;
-        const float4 q = *reinterpret_cast<const float4*>(p.pe + (size_t)jpos * N + n);
-        *reinterpret_cast<float4*>((float*)p.out + off) =
-            make_float4(v[0] + q.x, v[1] + q.y, v[2] + q.z, v[3] + q.w);
-      } else {
-        *reinterpret_cast<float4*>((float*)p.out + off) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-    }
-  }
+  staged_epilogue<BN, WN, NT8, EPI>(p, m0, n0, wm, wn, tid, acc, As0, As1, Bs0, Bs1);
 }
 
 template <int BN, int AMODE, int EPI>
@@ -611,6 +656,9 @@ int g_gemm256_force_bn = 0;  // tuning hook: 0 = automatic
 
 hipError_t launch_gemm256(const GemmArgs& a, int amode, int epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  // the epilogue copies 16-byte chunks of output rows
+  const int epc = (epi == EPI_STORE || epi == EPI_STORE_GELU) ? 8 : 4;
+  if (a.N % epc || a.ldo % epc || ((size_t)a.out & 15)) return hipErrorInvalidValue;
   const int bn = g_gemm256_force_bn ? g_gemm256_force_bn : pick_bn(a.M, a.N);
   switch (bn) {
     case 320: return dispatch<320>(a, amode, epi, s);
