@@ -89,8 +89,8 @@ __device__ __forceinline__ void lds_barrier() {
 // scattered rows, so storing them straight to memory writes 8- or 16-byte
 // pieces of many cache lines, which the memory system then writes back as
 // partial lines.  Instead the tile goes through LDS (the operand stages are
-// free once the k loop is over) in passes of PR rows: the waves owning those
-// rows write them (bias and GELU applied), then every thread copies 16-byte
+// free once the k loop is over) in passes of PR rows: the waves write their
+// share of the pass (bias and GELU applied), then every thread copies 16-byte
 // chunks of whole rows to memory, consecutive threads on consecutive chunks,
 // applying the residual or position add on the way.  The staged rows are
 // spread over the four largest stage arrays, RB rows each, with a row pitch
@@ -112,6 +112,12 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& p, int m0, int n
   constexpr int EPC = 16 / ES;             // elements per chunk
   constexpr int PER_THREAD = PR * CPR / NT;
   static_assert(PR * CPR % NT == 0, "whole chunks per thread");
+  // A pass takes HALF rows from each half of the tile (wm = 0: rows 0..127,
+  // wm = 1: 128..255), so every wave stages some rows in every pass and
+  // frees those accumulators early.
+  constexpr int HALF = PR / 2;
+  constexpr int IPP = HALF / 16;  // 16-row blocks per wave per pass
+  static_assert(HALF % 16 == 0 && RB % 16 == 0, "whole 16-row blocks per buffer");
   const int M = p.M, N = p.N;
   const int lane = tid & 63, lrow = lane & 15, g = lane >> 4;
   float4 bq[NTW];
@@ -121,14 +127,19 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& p, int m0, int n
     bq[j] = (p.bias && n < N) ? *reinterpret_cast<const float4*>(p.bias + n)
                               : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  // Have the bias in registers before any store: vector memory operations
+  // complete in issue order, so a bias load the compiler sinks into a later
+  // pass would wait for every store issued before it.
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) asm volatile("" ::"v"(bq[j].x), "v"(bq[j].y), "v"(bq[j].z), "v"(bq[j].w));
 #pragma unroll
   for (int pass = 0; pass < 256 / PR; ++pass) {
     lds_barrier();  // the k loop, or the previous pass's copy-out, is done with LDS
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int rowt = wm * 128 + 16 * i;  // first tile row of this 16-row block
-      if (rowt / PR != pass) continue;     // uniform over the wave
-      const int lr0 = rowt - pass * PR;
+      if (i / IPP != pass) continue;  // 16-row blocks i of this pass (compile time)
+      // staged row of the block's first row: the wm = 0 half of the pass, then wm = 1
+      const int lr0 = wm * HALF + 16 * (i - pass * IPP);
       const int bsel = lr0 / RB;
       char* base = (char*)(bsel == 0 ? lds0 : bsel == 1 ? lds1 : bsel == 2 ? lds2 : lds3) +
                    (lr0 % RB + lrow) * PITCH;
@@ -155,35 +166,50 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& p, int m0, int n
       }
     }
     lds_barrier();
+    // Copy-out in batches: every load of a batch (staged rows, residual or
+    // position rows) is issued before any of its stores, so a batch waits for
+    // the earlier stores once rather than once per chunk.
+    constexpr int SB = PER_THREAD % 2 == 0 ? PER_THREAD / 2 : PER_THREAD;
 #pragma unroll
-    for (int s = 0; s < PER_THREAD; ++s) {
-      const int q = tid + NT * s;
-      const int r = q / CPR;
-      const int c = q - r * CPR;
-      const int m = m0 + pass * PR + r;
-      const int n = n0 + c * EPC;
-      if (m >= M || n >= N) continue;
-      const int b = r / RB;
-      const char* src = (const char*)(b == 0 ? lds0 : b == 1 ? lds1 : b == 2 ? lds2 : lds3) +
-                        (r - b * RB) * PITCH + c * 16;
-      const u32x4_t d = *reinterpret_cast<const u32x4_t*>(src);
-      const size_t off = (size_t)m * p.ldo + n;
-      if (!F32) {
-        *reinterpret_cast<u32x4_t*>((bf16_t*)p.out + off) = d;
-      } else {
-        // (bit-cast the whole vector: a bit cast of one vector element reads element 0)
-        const f32x4_t f = __builtin_bit_cast(f32x4_t, d);
-        float4 v = make_float4(f[0], f[1], f[2], f[3]);
-        float4* o = reinterpret_cast<float4*>((float*)p.out + off);
-        if (EPI == EPI_RESID) {
-          const float4 x = *o;
-          v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
-        } else if (EPI == EPI_PE) {
-          const int jpos = p.rowmap[m] % p.tpc;
-          const float4 q4 = *reinterpret_cast<const float4*>(p.pe + (size_t)jpos * N + n);
-          v.x += q4.x; v.y += q4.y; v.z += q4.z; v.w += q4.w;
+    for (int s0 = 0; s0 < PER_THREAD; s0 += SB) {
+      u32x4_t d[SB];
+      float4 add[SB];
+      size_t off[SB];
+      bool ok[SB];
+#pragma unroll
+      for (int t = 0; t < SB; ++t) {
+        const int q = tid + NT * (s0 + t);
+        const int r = q / CPR;
+        const int c = q - r * CPR;
+        const int m = m0 + (r / HALF) * 128 + pass * HALF + r % HALF;
+        const int n = n0 + c * EPC;
+        ok[t] = m < M && n < N;
+        const int b = r / RB;
+        const char* src = (const char*)(b == 0 ? lds0 : b == 1 ? lds1 : b == 2 ? lds2 : lds3) +
+                          (r - b * RB) * PITCH + c * 16;
+        d[t] = *reinterpret_cast<const u32x4_t*>(src);
+        off[t] = (size_t)m * p.ldo + n;
+        add[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (ok[t]) {
+          if (EPI == EPI_RESID) {
+            add[t] = *reinterpret_cast<const float4*>((const float*)p.out + off[t]);
+          } else if (EPI == EPI_PE) {
+            const int jpos = p.rowmap[m] % p.tpc;
+            add[t] = *reinterpret_cast<const float4*>(p.pe + (size_t)jpos * N + n);
+          }
         }
-        *o = v;
+      }
+#pragma unroll
+      for (int t = 0; t < SB; ++t) {
+        if (!ok[t]) continue;
+        if (!F32) {
+          *reinterpret_cast<u32x4_t*>((bf16_t*)p.out + off[t]) = d[t];
+        } else {
+          // (bit-cast the whole vector: a bit cast of one vector element reads element 0)
+          const f32x4_t f = __builtin_bit_cast(f32x4_t, d[t]);
+          *reinterpret_cast<float4*>((float*)p.out + off[t]) =
+              make_float4(f[0] + add[t].x, f[1] + add[t].y, f[2] + add[t].z, f[3] + add[t].w);
+        }
       }
     }
   }
