@@ -36,8 +36,8 @@ __device__ __forceinline__ int kswz(int u, int j) {
 }
 
 __device__ __forceinline__ void frag_p(FragBF16& f, const float (&a)[4], const float (&b)[4]) {
-  f.v = bf16x8_t{to_bf16(a[0]), to_bf16(a[1]), to_bf16(a[2]), to_bf16(a[3]),
-                 to_bf16(b[0]), to_bf16(b[1]), to_bf16(b[2]), to_bf16(b[3])};
+  f.v = __builtin_bit_cast(bf16x8_t, u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                             pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])});
 }
 __device__ __forceinline__ void frag_p(FragF32& f, const float (&a)[4], const float (&b)[4]) {
 #pragma unroll

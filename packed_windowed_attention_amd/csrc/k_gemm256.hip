@@ -59,15 +59,6 @@ __device__ __forceinline__ lds_void* dma_dst(const u32x4_t* p) {
   return (lds_void*)(size_t)__builtin_amdgcn_readfirstlane(a);
 }
 
-__device__ __forceinline__ void store4(bf16_t* p, const float (&v)[4]) {
-  const bf16_t b0 = to_bf16(v[0]), b1 = to_bf16(v[1]), b2 = to_bf16(v[2]), b3 = to_bf16(v[3]);
-  const unsigned int lo = (unsigned int)__builtin_bit_cast(unsigned short, b0) |
-                          ((unsigned int)__builtin_bit_cast(unsigned short, b1) << 16);
-  const unsigned int hi = (unsigned int)__builtin_bit_cast(unsigned short, b2) |
-                          ((unsigned int)__builtin_bit_cast(unsigned short, b3) << 16);
-  *reinterpret_cast<u32x2_t*>(p) = u32x2_t{lo, hi};
-}
-
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding:
 // vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
 template <int n>
@@ -156,12 +147,8 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& p, int m0, int n
         if (F32) {
           *reinterpret_cast<f32x4_t*>(base + col * 4) = f32x4_t{v[0], v[1], v[2], v[3]};
         } else {
-          const bf16_t b0 = to_bf16(v[0]), b1 = to_bf16(v[1]), b2 = to_bf16(v[2]), b3 = to_bf16(v[3]);
           *reinterpret_cast<u32x2_t*>(base + col * 2) =
-              u32x2_t{(unsigned)__builtin_bit_cast(unsigned short, b0) |
-                          ((unsigned)__builtin_bit_cast(unsigned short, b1) << 16),
-                      (unsigned)__builtin_bit_cast(unsigned short, b2) |
-                          ((unsigned)__builtin_bit_cast(unsigned short, b3) << 16)};
+              u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
       }
     }

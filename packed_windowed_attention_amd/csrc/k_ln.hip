@@ -19,6 +19,14 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// four consecutive outputs in one store (8 bytes bf16, 16 bytes fp32)
+__device__ __forceinline__ void store_row4(bf16_t* p, float a, float b, float c, float d) {
+  *reinterpret_cast<u32x2_t*>(p) = u32x2_t{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+__device__ __forceinline__ void store_row4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
 template <typename T>
 __global__ __launch_bounds__(64 * LN_WAVES) void ln_kernel(const float* __restrict__ x,
                                                           const float* __restrict__ g,
@@ -57,10 +65,11 @@ __global__ __launch_bounds__(64 * LN_WAVES) void ln_kernel(const float* __restri
     const int c = lane + 64 * i;
     if (c < nv) {
       const float4 gg = g4[c], bb = b4[c];
-      yr[4 * c + 0] = from_f32<T>((v[i].x - mean) * rstd * gg.x + bb.x);
-      yr[4 * c + 1] = from_f32<T>((v[i].y - mean) * rstd * gg.y + bb.y);
-      yr[4 * c + 2] = from_f32<T>((v[i].z - mean) * rstd * gg.z + bb.z);
-      yr[4 * c + 3] = from_f32<T>((v[i].w - mean) * rstd * gg.w + bb.w);
+      const float o0 = (v[i].x - mean) * rstd * gg.x + bb.x;
+      const float o1 = (v[i].y - mean) * rstd * gg.y + bb.y;
+      const float o2 = (v[i].z - mean) * rstd * gg.z + bb.z;
+      const float o3 = (v[i].w - mean) * rstd * gg.w + bb.w;
+      store_row4(yr + 4 * c, o0, o1, o2, o3);
     }
   }
 }

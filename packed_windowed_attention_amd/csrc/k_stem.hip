@@ -27,9 +27,8 @@ template <typename T>
 __device__ __forceinline__ void store8(T* p, const float (&v)[8]);
 template <>
 __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float (&v)[8]) {
-  bf16x8_t b = {to_bf16(v[0]), to_bf16(v[1]), to_bf16(v[2]), to_bf16(v[3]),
-                to_bf16(v[4]), to_bf16(v[5]), to_bf16(v[6]), to_bf16(v[7])};
-  *reinterpret_cast<bf16x8_t*>(p) = b;
+  *reinterpret_cast<u32x4_t*>(p) = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
 }
 template <>
 __device__ __forceinline__ void store8<float>(float* p, const float (&v)[8]) {
