@@ -66,6 +66,14 @@ __device__ __forceinline__ void frag_v(FragF32& f, const float* p0, const float*
   f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
 }
 
+// four consecutive outputs in one store (8 bytes bf16, 16 bytes fp32)
+__device__ __forceinline__ void store_quad(bf16_t* p, float a, float b, float c, float d) {
+  *reinterpret_cast<u32x2_t*>(p) = u32x2_t{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+__device__ __forceinline__ void store_quad(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
 template <typename T>
 __global__ __launch_bounds__(ATT_THREADS) void attn_kernel(const T* __restrict__ qkv,
                                                           T* __restrict__ o,
@@ -86,67 +94,105 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_kernel(const T* __restrict__
   const int h = blockIdx.x - (blockIdx.x / H) * H;
   const int s0 = cu[w];
   const int L = cu[w + 1] - s0;
-  const int Lp = (L + 31) & ~31;
   const size_t ld = 3 * (size_t)d;
   const T* qb = qkv + (size_t)s0 * ld + (size_t)h * 64;
   const T* kb = qb + d;
   const T* vb = qb + 2 * (size_t)d;
 
-  for (int idx = tid; idx < Lp * UR; idx += ATT_THREADS) {
-    const int j = idx / UR, u = idx - j * UR;
-    const u32x4_t kv = j < L ? ldg_unit(kb + (size_t)j * ld + u * E) : zero_unit();
-    Ks[j * UR + kswz<T>(u, j)] = kv;
-    const u32x4_t vv = j < L ? ldg_unit(vb + (size_t)j * ld + u * E) : zero_unit();
-    T tmp[E];
-    __builtin_memcpy(tmp, &vv, 16);
+  // Every global load of the workgroup is issued before any is used: thread t
+  // takes unit u = t % UR of the RPT consecutive key rows starting at
+  // RPT * (t / UR) (K and V), and each wave the Q fragments of its query tiles
+  // wave and wave + 4.  Then K goes to LDS unit by unit and V transposed, RPT
+  // rows at a time (one 8- or 32-byte write per element of the unit).
+  constexpr int RPT = LMAX * UR / ATT_THREADS;  // key rows per thread: 4 (bf16), 8 (fp32)
+  const int ku = tid % UR;
+  const int kj0 = RPT * (tid / UR);
+  u32x4_t kreg[RPT], vreg[RPT];
 #pragma unroll
-    for (int e = 0; e < E; ++e) Vt[(u * E + e) * VS + j] = tmp[e];
+  for (int r = 0; r < RPT; ++r) {
+    const int j = kj0 + r;
+    kreg[r] = j < L ? ldg_unit(kb + (size_t)j * ld + ku * E) : zero_unit();
+    vreg[r] = j < L ? ldg_unit(vb + (size_t)j * ld + ku * E) : zero_unit();
+  }
+  constexpr int QU = E == 8 ? 2 : 4;  // Q units per lane per query tile
+  u32x4_t qreg[2][QU];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = (wave + 4 * q) * 16 + lrow;
+#pragma unroll
+    for (int s = 0; s < QU; ++s) {
+      // bf16: units 4 s' + g of k-half s'; fp32: units 8 s' + 2 g (+1)
+      const int u = E == 8 ? 4 * s + g : 8 * (s >> 1) + 2 * g + (s & 1);
+      qreg[q][s] = i < L ? ldg_unit(qb + (size_t)i * ld + u * E) : zero_unit();
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) Ks[(kj0 + r) * UR + kswz<T>(ku, kj0 + r)] = kreg[r];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    T col[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      T tmp[E];
+      __builtin_memcpy(tmp, &vreg[r], 16);
+      col[r] = tmp[e];
+    }
+    T* dst = &Vt[(ku * E + e) * VS + kj0];
+    if (E == 8) {
+      u32x2_t w2;
+      __builtin_memcpy(&w2, col, 8);
+      *reinterpret_cast<u32x2_t*>(dst) = w2;
+    } else {
+      u32x4_t w4[2];
+      __builtin_memcpy(w4, col, 32);
+      reinterpret_cast<u32x4_t*>(dst)[0] = w4[0];
+      reinterpret_cast<u32x4_t*>(dst)[1] = w4[1];
+    }
   }
   __syncthreads();
 
-  const int JT = Lp >> 4;
   // scores in log2 units: softmax(s / 8) = 2^(s log2(e) / 8 - max) / sum
   const float c = 0.125f * 1.44269504088896341f;
-  for (int it = wave; it * 16 < L; it += ATT_THREADS / 64) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int it = wave + 4 * q;
+    if (it * 16 >= L) break;
     const int i = it * 16 + lrow;
     Frag qf[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const T* qp = qb + (size_t)i * ld + 32 * s + 8 * g;
-      if (E == 8) {
-        frag_from_units(qf[s], i < L ? ldg_unit(qp) : zero_unit(), zero_unit());
-      } else {
-        frag_from_units(qf[s], i < L ? ldg_unit(qp) : zero_unit(),
-                        i < L ? ldg_unit(qp + 4) : zero_unit());
+      if (E == 8) frag_from_units(qf[s], qreg[q][s], zero_unit());
+      else frag_from_units(qf[s], qreg[q][2 * s], qreg[q][2 * s + 1]);
+    }
+    // S^T = K Q^T over all LMAX key rows (rows past the window are zero in LDS
+    // and masked below): straight-line code, so every fragment read is issued
+    // ahead of the matrix instructions that use it
+    Frag kf[8][2];
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) {
+      const int jr = jt * 16 + lrow;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (E == 8) {
+          frag_from_units(kf[jt][s], Ks[jr * UR + kswz<T>(4 * s + g, jr)], zero_unit());
+        } else {
+          const int u = 8 * s + 2 * g;
+          frag_from_units(kf[jt][s], Ks[jr * UR + kswz<T>(u, jr)], Ks[jr * UR + kswz<T>(u + 1, jr)]);
+        }
       }
     }
     float t[8][4];
     float mx = -INFINITY;
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt) {
-      if (jt < JT) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        const int jr = jt * 16 + lrow;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      mma16_k32(acc, kf[jt][0], qf[0]);
+      mma16_k32(acc, kf[jt][1], qf[1]);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          Frag kf;
-          if (E == 8) {
-            frag_from_units(kf, Ks[jr * UR + kswz<T>(4 * s + g, jr)], zero_unit());
-          } else {
-            const int u = 8 * s + 2 * g;
-            frag_from_units(kf, Ks[jr * UR + kswz<T>(u, jr)], Ks[jr * UR + kswz<T>(u + 1, jr)]);
-          }
-          mma16_k32(acc, kf, qf[s]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = jt * 16 + 4 * g + r;
-          t[jt][r] = j < L ? acc[r] * c : -INFINITY;
-          mx = fmaxf(mx, t[jt][r]);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) t[jt][r] = -INFINITY;
+      for (int r = 0; r < 4; ++r) {
+        const int j = jt * 16 + 4 * g + r;
+        t[jt][r] = j < L ? acc[r] * c : -INFINITY;
+        mx = fmaxf(mx, t[jt][r]);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -156,36 +202,42 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_kernel(const T* __restrict__
     for (int jt = 0; jt < 8; ++jt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        t[jt][r] = jt < JT ? exp2f(t[jt][r] - mx) : 0.f;
+        t[jt][r] = __builtin_amdgcn_exp2f(t[jt][r] - mx);  // masked keys: 2^-inf = 0
         sum += t[jt][r];
       }
     sum += __shfl_xor(sum, 16, 64);
     sum += __shfl_xor(sum, 32, 64);
 
+    // O^T = V^T P^T, V^T fragments read ahead in two batches of 8
     f32x4_t oacc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      if (2 * tt < JT) {
+    for (int half = 0; half < 2; ++half) {
+      Frag vf[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const T* vrow = Vt + (dt * 16 + lrow) * VS + 32 * (2 * half + u) + 4 * g;
+          frag_v(vf[u][dt], vrow, vrow + 16);
+        }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int tt = 2 * half + u;
         Frag pf;
         frag_p(pf, t[2 * tt], t[2 * tt + 1]);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const T* vrow = Vt + (dt * 16 + lrow) * VS + 32 * tt + 4 * g;
-          Frag vf;
-          frag_v(vf, vrow, vrow + 16);
-          mma16_k32(oacc[dt], vf, pf);
-        }
+        for (int dt = 0; dt < 4; ++dt) mma16_k32(oacc[dt], vf[u][dt], pf);
       }
     }
     if (i < L) {
-      const float inv = 1.0f / sum;
+      const float inv = __builtin_amdgcn_rcpf(sum);
       T* orow = o + (size_t)(s0 + i) * d + (size_t)h * 64;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) orow[dt * 16 + 4 * g + r] = from_f32<T>(oacc[dt][r] * inv);
+        store_quad(orow + dt * 16 + 4 * g, oacc[dt][0] * inv, oacc[dt][1] * inv,
+                   oacc[dt][2] * inv, oacc[dt][3] * inv);
     }
   }
 }

@@ -12,11 +12,14 @@ namespace {
 
 constexpr int LN_WAVES = 4;
 constexpr int LN_MAXV = 8;  // float4 per lane: d <= 2048
+constexpr int LN_RPW = 1;   // rows per wave (2 or 4 measured slower)
 
-__device__ __forceinline__ float wave_sum(float v) {
+// butterfly sums over the wavefront of LN_RPW independent values at once
+__device__ __forceinline__ void wave_sum_n(float (&v)[LN_RPW]) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+    for (int k = 0; k < LN_RPW; ++k) v[k] += __shfl_xor(v[k], o, 64);
 }
 
 // four consecutive outputs in one store (8 bytes bf16, 16 bytes fp32)
@@ -33,43 +36,66 @@ __global__ __launch_bounds__(64 * LN_WAVES) void ln_kernel(const float* __restri
                                                           const float* __restrict__ b,
                                                           T* __restrict__ y, int rows, int d,
                                                           float eps) {
+  // LN_RPW rows per wave, loaded together so that their loads and their
+  // reductions overlap
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * LN_WAVES + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  const int row0 = (blockIdx.x * LN_WAVES + (threadIdx.x >> 6)) * LN_RPW;
+  if (row0 >= rows) return;
   const int nv = d >> 2;
-  const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * d);
-  float4 v[LN_MAXV];
-  float s = 0.f;
+  float4 v[LN_RPW][LN_MAXV];
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
-    const int c = lane + 64 * i;
-    v[i] = c < nv ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-    s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
-  }
-  const float mean = wave_sum(s) / (float)d;
-  float q = 0.f;
+  for (int k = 0; k < LN_RPW; ++k) {
+    const float4* xr = reinterpret_cast<const float4*>(x + (size_t)(row0 + k) * d);
+    const bool live = row0 + k < rows;
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nv) {
-      const float a0 = v[i].x - mean, a1 = v[i].y - mean, a2 = v[i].z - mean, a3 = v[i].w - mean;
-      q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+    for (int i = 0; i < LN_MAXV; ++i) {
+      const int c = lane + 64 * i;
+      v[k][i] = (live && c < nv) ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
-  const float rstd = rsqrtf(wave_sum(q) / (float)d + eps);
-  T* yr = y + (size_t)row * d;
+  float mean[LN_RPW], rstd[LN_RPW];
+#pragma unroll
+  for (int k = 0; k < LN_RPW; ++k) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) s += (v[k][i].x + v[k][i].y) + (v[k][i].z + v[k][i].w);
+    mean[k] = s;
+  }
+  wave_sum_n(mean);
+#pragma unroll
+  for (int k = 0; k < LN_RPW; ++k) {
+    mean[k] /= (float)d;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nv) {
+        const float a0 = v[k][i].x - mean[k], a1 = v[k][i].y - mean[k];
+        const float a2 = v[k][i].z - mean[k], a3 = v[k][i].w - mean[k];
+        q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+      }
+    }
+    rstd[k] = q;
+  }
+  wave_sum_n(rstd);
   const float4* g4 = reinterpret_cast<const float4*>(g);
   const float4* b4 = reinterpret_cast<const float4*>(b);
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nv) {
-      const float4 gg = g4[c], bb = b4[c];
-      const float o0 = (v[i].x - mean) * rstd * gg.x + bb.x;
-      const float o1 = (v[i].y - mean) * rstd * gg.y + bb.y;
-      const float o2 = (v[i].z - mean) * rstd * gg.z + bb.z;
-      const float o3 = (v[i].w - mean) * rstd * gg.w + bb.w;
-      store_row4(yr + 4 * c, o0, o1, o2, o3);
+  for (int k = 0; k < LN_RPW; ++k) {
+    if (row0 + k >= rows) break;
+    const float rs = rsqrtf(rstd[k] / (float)d + eps);
+    T* yr = y + (size_t)(row0 + k) * d;
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nv) {
+        const float4 gg = g4[c], bb = b4[c];
+        const float o0 = (v[k][i].x - mean[k]) * rs * gg.x + bb.x;
+        const float o1 = (v[k][i].y - mean[k]) * rs * gg.y + bb.y;
+        const float o2 = (v[k][i].z - mean[k]) * rs * gg.z + bb.z;
+        const float o3 = (v[k][i].w - mean[k]) * rs * gg.w + bb.w;
+        store_row4(yr + 4 * c, o0, o1, o2, o3);
+      }
     }
   }
 }
@@ -80,7 +106,7 @@ hipError_t launch_layernorm(const float* x, const float* g, const float* b, void
                             float eps, aut_dtype dt, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (d % 4 || d > 4 * 64 * LN_MAXV) return hipErrorInvalidValue;
-  dim3 grid((T + LN_WAVES - 1) / LN_WAVES);
+  dim3 grid((T + LN_WAVES * LN_RPW - 1) / (LN_WAVES * LN_RPW));
   if (dt == AUT_BF16)
     hipLaunchKernelGGL(ln_kernel<bf16_t>, grid, dim3(64 * LN_WAVES), 0, s, x, g, b, (bf16_t*)y, T,
                        d, eps);
