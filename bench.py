@@ -205,6 +205,10 @@ def main():
     name = args.workload
     log(f"generating workload {name}")
     cfg_d, lens, feats, P = si.workload(name)
+    # conv-stem batch: as many chunks per launch as the kernels' 32-bit buffer
+    # offsets allow (the library caps it); a memory knob with no effect on the
+    # results, and fewer, fuller launches
+    cfg_d = dict(cfg_d, conv_chunksize=max(cfg_d["conv_chunksize"], 4096))
     dtype = cfg_d["dtype"]
     cfg = aut.config(cfg_d)
     dev = {k: torch.from_numpy(v).cuda() for k, v in P.items()}

@@ -640,12 +640,13 @@ hipError_t dispatch(const GemmArgs& a, int amode, int epi, hipStream_t s) {
 
 // Column tile for an N: the candidate with the best estimated throughput,
 // i.e. tile-slot use on 256 CUs (partly empty last round, columns past N)
-// times the measured relative speed of the kernel (the eight-wave kernels for
-// BN = 320 and 256 move about 25% fewer bytes per flop and run that much
-// faster per tile); ties to the first candidate.
+// times the measured relative speed of the kernel per tile-slot (eight-wave
+// 256 x 320 / 256 x 256 tiles run ~1.3x the four-wave 256 x 160 ones on the
+// layer GEMMs and the conv3 implicit GEMM; 256 x 128 ~0.87x); ties to the
+// first candidate.
 int pick_bn(int M, int N) {
   const int cands[4] = {320, 256, 160, 128};
-  const double speed[4] = {1.25, 1.25, 1.0, 1.0};
+  const double speed[4] = {1.3, 1.3, 1.0, 0.87};
   const int nM = (M + BM - 1) / BM;
   int best = 320;
   double best_eff = -1.0;

@@ -136,6 +136,22 @@ def test_large_sampled_windows(name):
         check(y[r0:r0 + ref.shape[0]], ref, "bf16", f"{name} window {w} (rows {r0}+{ref.shape[0]})")
 
 
+def test_wide_bench_launch_config():
+    """The wide workload in the launch configuration bench.py times (conv-stem
+    batches as large as the library allows), seeded sample of windows."""
+    cfg_d, lens, feats, P = workload("wide")
+    cfg_d = dict(cfg_d, conv_chunksize=4096)
+    print("case: wide bf16, bench launch configuration, sampled windows", flush=True)
+    y, pl = forward(cfg_d, lens, feats, P)
+    opl = oracle.plan(lens, cfg_d)
+    assert pl.copy()[1] == opl["cu_seqlens"]
+    assert np.isfinite(y).all()
+    wins = sample_windows(opl, seed=si.workload_seed("wide") + 7, n_random=2)
+    res = oracle.forward_windows(feats, lens, P, cfg_d, wins)
+    for w, (r0, ref) in res.items():
+        check(y[r0:r0 + ref.shape[0]], ref, "bf16", f"wide/bench window {w} (rows {r0}+{ref.shape[0]})")
+
+
 def test_window_isolation_bitwise():
     """openarchlab "1A", section 4: change one window's spectrogram, every other
     window's output must not move at all (0.00e+00)."""
