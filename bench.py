@@ -127,6 +127,35 @@ def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_mib,
     print("\n".join(out))
 
 
+def stream_latency(aut, torch, cfg, packed, dtype, feats, steps, append=100):
+    """Incremental encode of one live request (the workload's first request's
+    mel, repeated as needed) receiving `append` frames per step: each step
+    re-encodes from the first non-final window (aut_encode_stream). Reports the
+    per-step latency; not part of `value`."""
+    mel = np.ascontiguousarray(np.nan_to_num(feats[0], nan=-4.0))
+    total = steps * append
+    reps = -(-total // mel.shape[1])
+    full = np.tile(mel, (1, reps))[:, :total]
+    fdev = torch.from_numpy(np.ascontiguousarray(full)).cuda()
+    rows_max = aut.stream_plan(cfg, total, 0)["rows"]
+    out = torch.empty((rows_max, cfg.output_dim), dtype=torch.float32, device="cuda")
+    ws = aut.stream_workspace(cfg, total, dtype)
+    times = []
+    wf = 0
+    for k in range(1, steps + 1):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        wf = aut.encode_stream(cfg, fdev, k * append, wf, packed, dtype, out, ws)
+        torch.cuda.synchronize()
+        times.append(1e3 * (time.perf_counter() - t0))
+    t = np.array(times[1:])
+    return {"append_frames": append, "steps": steps, "request_seconds": total / 100.0,
+            "step_ms_p50": float(np.percentile(t, 50)), "step_ms_p95": float(np.percentile(t, 95)),
+            "rtf_p50": float(np.percentile(t, 50)) / (1e3 * append / 100.0),
+            "note": "wall time per step incl. plan upload and one stream sync; one request, "
+                    "re-encodes at most one 8 s window plus the new chunks"}
+
+
 def cpu_baseline(name, cfg_d, lens, feats, P, n_windows):
     """The float64 oracle on a bounded sample of the same workload's windows."""
     import oracle
@@ -163,6 +192,8 @@ def main():
     ap.add_argument("--workload", default="wide", choices=list(si.WORKLOADS))
     ap.add_argument("--cpu-windows", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stream-steps", type=int, default=30,
+                    help="1 s appends timed for the incremental-encode latency (0: skip)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without per-launch HIP events (no roofline)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -309,6 +340,9 @@ def main():
         allf = sum(s["flops"] for c, s in stats.items() if c != "layernorm")
         res["mfma_frac_step"] = allf / args.steps / (ms_per_step / 1e3) / 1e12 / peak
         res["attention_gbs"] = a["bytes"] / (a["total_ms"] / 1e3) / 1e9 if a["total_ms"] else None
+    if args.stream_steps > 0:
+        res["stream"] = stream_latency(aut, torch, cfg, packed, dtype, feats, args.stream_steps)
+        log(f"stream: {res['stream']['step_ms_p50']:.3f} ms per 1 s append (p50)")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on sampled windows)")
         res["cpu_baseline"] = cpu_baseline(name, cfg_d, lens, feats, P, args.cpu_windows)

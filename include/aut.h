@@ -206,6 +206,51 @@ aut_status aut_encode_packed(const aut_config* cfg, const aut_plan_t* plan, cons
                              const void* packed, aut_dtype dtype, float* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Incremental (streaming) encode of one live request.
+ *
+ * A window covers its own n_window_infer frames (8 chunks; m-star
+ * AuTEncoderConfig.window_lengths: windows never span requests or other
+ * frames) and attention is block-diagonal over windows (m-star module
+ * summary; openarchlab "1A", section 4: perturbing one window leaves every
+ * other window's output unchanged).  So once a request holds all
+ * n_window_infer frames of a window, that window's output rows are final, and
+ * a caller that appends audio re-encodes only the frames from the first
+ * window that was not final at its previous step.  The result equals the
+ * batch encode of the whole request, bit for bit.
+ * ------------------------------------------------------------------------ */
+
+/* Host-only arithmetic for one step.  frames_total >= 0 frames received so
+ * far; windows_final >= 0 windows already emitted as final (at most the
+ * complete windows in frames_total, else AUT_ERR_INVALID_ARG).  Outputs (any
+ * may be NULL):
+ *   frame_begin         = windows_final * n_window_infer, first frame to encode;
+ *   row_begin           = windows_final * window tokens, its first output row;
+ *   rows                = output rows from row_begin to the request's end
+ *                         (0 when nothing is left to encode);
+ *   windows_final_after = complete windows in frames_total. */
+aut_status aut_stream_plan(const aut_config* cfg, int32_t frames_total, int32_t windows_final,
+                           int32_t* frame_begin, int32_t* row_begin, int32_t* rows,
+                           int32_t* windows_final_after);
+
+/* Workspace bytes that cover every step of a request of up to max_frames
+ * frames (the workspace of a one-request plan of max_frames frames). */
+aut_status aut_stream_workspace_bytes(const aut_config* cfg, int32_t max_frames, aut_dtype dtype,
+                                      size_t* bytes);
+
+/* One step: encodes frames [frame_begin, frames_total) of the request whose
+ * log-mel is `features` (device fp32 [num_mel_bins, T_max], time fastest,
+ * T_max >= frames_total) and writes output rows [row_begin, row_begin + rows)
+ * of `out` (device fp32, the request's output, [tokens(frames_total),
+ * output_dim] or longer).  Rows before row_begin are not touched.  The
+ * workspace must hold aut_stream_workspace_bytes for frames_total frames.
+ * Stream use and synchronisation as aut_encode.  *windows_final_after (may
+ * be NULL) receives the new count of final windows. */
+aut_status aut_encode_stream(const aut_config* cfg, const float* features, int32_t T_max,
+                             int32_t frames_total, int32_t windows_final, const void* packed,
+                             aut_dtype dtype, float* out, void* workspace, size_t workspace_bytes,
+                             void* stream, int32_t* windows_final_after);
+
 /* Kernel classes for the optional per-launch timing below. */
 typedef enum {
   AUT_K_CONV1 = 0,     /* conv1 (+GELU), fp32 vector ALU */

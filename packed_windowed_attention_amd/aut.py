@@ -70,6 +70,11 @@ SIGNATURES = {
                              c_void_p, c_void_p, c_size_t, c_void_p]),
     "aut_encode_packed": (c_int, [POINTER(AutConfig), c_void_p, c_void_p, c_void_p, c_int,
                                   c_void_p, c_void_p, c_size_t, c_void_p]),
+    "aut_stream_plan": (c_int, [POINTER(AutConfig), c_int32, c_int32, POINTER(c_int32),
+                                POINTER(c_int32), POINTER(c_int32), POINTER(c_int32)]),
+    "aut_stream_workspace_bytes": (c_int, [POINTER(AutConfig), c_int32, c_int, POINTER(c_size_t)]),
+    "aut_encode_stream": (c_int, [POINTER(AutConfig), c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                  c_int, c_void_p, c_void_p, c_size_t, c_void_p, POINTER(c_int32)]),
     "aut_profile_enable": (c_int, [c_int]),
     "aut_profile_collect": (c_int, [POINTER(AutKernelStats)]),
     "aut_last_error": (c_char_p, []),
@@ -279,6 +284,37 @@ def encode_packed(cfg: AutConfig, pl: Plan, hidden, packed, dtype, out, ws, stre
                                    _dtype(dtype), _ptr(out), _ptr(ws), ws.numel(),
                                    _stream_ptr(stream)))
     return out
+
+
+def stream_plan(cfg: AutConfig, frames_total: int, windows_final: int) -> dict:
+    """aut_stream_plan: frame/row range of one incremental-encode step."""
+    f0, r0, rows, after = c_int32(), c_int32(), c_int32(), c_int32()
+    _check(lib().aut_stream_plan(byref(cfg), int(frames_total), int(windows_final), byref(f0),
+                                 byref(r0), byref(rows), byref(after)))
+    return dict(frame_begin=f0.value, row_begin=r0.value, rows=rows.value,
+                windows_final_after=after.value)
+
+
+def stream_workspace(cfg: AutConfig, max_frames: int, dtype, device="cuda"):
+    """Workspace for every step of a request of up to max_frames frames."""
+    import torch
+    n = c_size_t()
+    _check(lib().aut_stream_workspace_bytes(byref(cfg), int(max_frames), _dtype(dtype), byref(n)))
+    return torch.empty(max(1, n.value), dtype=torch.uint8, device=device)
+
+
+def encode_stream(cfg: AutConfig, features, frames_total: int, windows_final: int, packed, dtype,
+                  out, ws, stream=None) -> int:
+    """aut_encode_stream: re-encode a live request from its first non-final
+    window; features [mel, T_max] fp32 on the device, out the request's output
+    rows.  Returns the new count of final windows."""
+    if str(features.dtype) != "torch.float32" or features.dim() != 2 or not features.is_contiguous():
+        raise ValueError("features must be a contiguous float32 [mel, T_max] tensor")
+    after = c_int32()
+    _check(lib().aut_encode_stream(byref(cfg), _ptr(features), features.shape[1], int(frames_total),
+                                   int(windows_final), _ptr(packed), _dtype(dtype), _ptr(out),
+                                   _ptr(ws), ws.numel(), _stream_ptr(stream), byref(after)))
+    return after.value
 
 
 def profile_enable(on: bool):

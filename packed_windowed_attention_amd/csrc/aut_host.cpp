@@ -791,6 +791,81 @@ extern "C" aut_status aut_encode(const aut_config* cfg, const float* features, i
 }
 
 // ---------------------------------------------------------------------------
+// incremental (streaming) encode of one request
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// output rows of a request of L frames: full chunks of w3 tokens plus the
+// three stride-2 halvings of a partial chunk's frames
+int64_t request_tokens(const Geometry& g, int64_t L) {
+  const int64_t full = L / g.cf;
+  const int rem = (int)(L - full * g.cf);
+  return full * g.w3 + (rem ? half_up(half_up(half_up(rem))) : 0);
+}
+
+}  // namespace
+
+extern "C" aut_status aut_stream_plan(const aut_config* cfg, int32_t frames_total,
+                                      int32_t windows_final, int32_t* frame_begin,
+                                      int32_t* row_begin, int32_t* rows,
+                                      int32_t* windows_final_after) {
+  aut_status st = aut_config_check(cfg);
+  if (st != AUT_OK) return st;
+  if (frames_total < 0) return fail(AUT_ERR_INVALID_ARG, "frames_total = %d < 0", frames_total);
+  const Geometry g = aut::geometry(*cfg);
+  const int fpw = g.cf * g.chunks_per_window;  // frames per window (n_window_infer)
+  const int complete = frames_total / fpw;
+  if (windows_final < 0 || windows_final > complete)
+    return fail(AUT_ERR_INVALID_ARG, "windows_final = %d outside [0, %d] for %d frames",
+                windows_final, complete, frames_total);
+  const int64_t f0 = (int64_t)windows_final * fpw;
+  const int64_t r0 = (int64_t)windows_final * g.window_tokens;
+  if (frame_begin) *frame_begin = (int32_t)f0;
+  if (row_begin) *row_begin = (int32_t)r0;
+  if (rows) *rows = (int32_t)(request_tokens(g, frames_total) - r0);
+  if (windows_final_after) *windows_final_after = complete;
+  return AUT_OK;
+}
+
+extern "C" aut_status aut_stream_workspace_bytes(const aut_config* cfg, int32_t max_frames,
+                                                 aut_dtype dtype, size_t* bytes) {
+  if (!bytes) return fail(AUT_ERR_INVALID_ARG, "bytes is NULL");
+  if (max_frames < 0) return fail(AUT_ERR_INVALID_ARG, "max_frames = %d < 0", max_frames);
+  aut_plan_t* plan = nullptr;
+  aut_status st = aut_plan(cfg, &max_frames, 1, &plan);
+  if (st != AUT_OK) return st;
+  st = aut_workspace_bytes(cfg, plan, dtype, bytes);
+  aut_plan_destroy(plan);
+  return st;
+}
+
+extern "C" aut_status aut_encode_stream(const aut_config* cfg, const float* features,
+                                        int32_t T_max, int32_t frames_total,
+                                        int32_t windows_final, const void* packed, aut_dtype dt,
+                                        float* out, void* ws, size_t ws_bytes, void* stream,
+                                        int32_t* windows_final_after) {
+  int32_t f0 = 0, r0 = 0, rows = 0, after = 0;
+  aut_status st = aut_stream_plan(cfg, frames_total, windows_final, &f0, &r0, &rows, &after);
+  if (st != AUT_OK) return st;
+  if (frames_total > T_max)
+    return fail(AUT_ERR_INVALID_ARG, "frames_total = %d exceeds T_max = %d", frames_total, T_max);
+  if (rows > 0) {
+    if (!features) return fail(AUT_ERR_INVALID_ARG, "features is NULL");
+    if (!out) return fail(AUT_ERR_INVALID_ARG, "out is NULL");
+    // the frames from f0 on form a request of their own: same mel rows (row
+    // stride T_max), chunk-aligned start, so the same chunks, windows and
+    // chunk-local positions as in the whole request
+    const int32_t len = frames_total - f0;
+    st = aut_encode(cfg, features + f0, T_max, &len, 1, packed, dt,
+                    out + (size_t)r0 * cfg->output_dim, ws, ws_bytes, stream);
+    if (st != AUT_OK) return st;
+  }
+  if (windows_final_after) *windows_final_after = after;
+  return AUT_OK;
+}
+
+// ---------------------------------------------------------------------------
 // timing and errors
 // ---------------------------------------------------------------------------
 

@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = aut.lib()
     names = declared_functions()
-    assert len(names) == len(aut.SIGNATURES) == 17
+    assert len(names) == len(aut.SIGNATURES) == 20
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(aut.SIGNATURES), "binding and header disagree"
@@ -152,3 +152,50 @@ def test_encode_argument_checks_before_launch():
     z = (ctypes.c_int32 * 1)(0)
     assert L.aut_encode(ctypes.byref(cfg), None, 0, z, 1, None, 0, None, None, 0, None) == 0
     assert L.aut_encode(ctypes.byref(cfg), None, 0, z, 0, None, 0, None, None, 0, None) == 0
+
+
+def _oracle_tokens(L, cfg_d):
+    return oracle.plan([L], cfg_d)["tokens_per_request"][0]
+
+
+def test_stream_plan_vs_oracle():
+    """aut_stream_plan against the oracle's plan: window k of a request starts at
+    frame 800 k and row 104 k; the frames from there form a request of their own
+    with the remaining rows (chunk-aligned start)."""
+    cfg_d = si.model_config("wide")
+    cfg = aut.config(cfg_d)
+    rng = np.random.default_rng(5)
+    lens = [0, 1, 99, 100, 101, 799, 800, 801, 1599, 1600, 1601, 2630] + [int(x) for x in rng.integers(0, 12000, 30)]
+    for L in lens:
+        opl = oracle.plan([L], cfg_d)
+        cu = opl["cu_seqlens"]
+        complete = L // 800
+        assert complete == sum(1 for w in range(len(cu) - 1) if cu[w + 1] - cu[w] == 104 and (w + 1) * 800 <= L)
+        for wf in sorted({0, complete // 2, complete}):
+            sp = aut.stream_plan(cfg, L, wf)
+            assert sp["frame_begin"] == 800 * wf
+            assert sp["row_begin"] == (cu[wf] if wf < len(cu) else cu[-1])
+            assert sp["rows"] == _oracle_tokens(L, cfg_d) - sp["row_begin"]
+            assert sp["rows"] == _oracle_tokens(L - 800 * wf, cfg_d)
+            assert sp["windows_final_after"] == complete
+
+
+def test_stream_plan_errors():
+    cfg = aut.config(si.model_config("wide"))
+    for L, wf in ((100, 1), (1599, 2), (-1, 0), (800, -1)):
+        with pytest.raises(RuntimeError) as e:
+            aut.stream_plan(cfg, L, wf)
+        assert "AUT_ERR_INVALID_ARG" in str(e.value)
+
+
+def test_stream_workspace_covers_each_step():
+    """The one-request workspace for max_frames covers the plan of any step."""
+    cfg_d = si.model_config("rag")
+    cfg = aut.config(cfg_d)
+    lib = aut.lib()
+    import ctypes as ct
+    for mx in (1, 800, 2630, 12000):
+        n = ct.c_size_t()
+        assert lib.aut_stream_workspace_bytes(ct.byref(cfg), mx, aut.DTYPES["bf16"], ct.byref(n)) == 0
+        for L in (1, mx // 3, mx):
+            assert aut.workspace_bytes(cfg, aut.plan(cfg, [L]), "bf16") <= n.value

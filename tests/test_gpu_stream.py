@@ -1,0 +1,71 @@
+"""Incremental (streaming) encode through the C ABI: a live request whose
+audio arrives in pieces, re-encoded from its first non-final window at each
+step, ends bit-identical to the batch encode, and rows that are final are
+never rewritten (windows are independent: m-star module summary; openarchlab
+"1A", section 4)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synth_inputs as si
+from gpu_common import forward, pack, small_cfg, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+ARRIVALS = [150, 420, 800, 1010, 1650, 2400, 2630]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_stream_equals_batch(dtype):
+    from packed_windowed_attention_amd import aut
+    torch = torch_mod()
+    cfg_d = small_cfg(dtype)
+    L = ARRIVALS[-1]
+    lens = np.array([L])
+    feats = si.mel_features(lens, seed=31)
+    P = si.params(cfg_d, seed=31, std=0.05)
+    cfg, packed = pack(cfg_d, P)
+    print(f"case: stream {dtype} L={L} arrivals={ARRIVALS}", flush=True)
+    y_batch, _ = forward(cfg_d, lens, feats, packed=packed, cfg=cfg)
+    T = y_batch.shape[0]
+    T_max = feats.shape[2]
+    # frames not yet arrived hold NaN: any read of them would show in the output
+    fbuf = torch.full((cfg_d["num_mel_bins"], T_max), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((T, cfg_d["output_dim"]), float("nan"), dtype=torch.float32, device="cuda")
+    ws = aut.stream_workspace(cfg, L, dtype)
+    wf = 0
+    prev = out.cpu().numpy()
+    for n in ARRIVALS:
+        fbuf[:, :n] = torch.from_numpy(np.ascontiguousarray(feats[0, :, :n])).cuda()
+        sp = aut.stream_plan(cfg, n, wf)
+        wf_new = aut.encode_stream(cfg, fbuf, n, wf, packed, dtype, out, ws)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        r0, r1 = sp["row_begin"], sp["row_begin"] + sp["rows"]
+        print(f"[stream {dtype}] frames {n}: rows {r0}..{r1}, final windows {wf} -> {wf_new}", flush=True)
+        assert np.isfinite(o[r0:r1]).all()
+        # rows of windows already final were not touched
+        np.testing.assert_array_equal(o[:r0], prev[:r0])
+        # rows final now equal the batch result bit for bit
+        rf = sp["row_begin"] + 104 * (wf_new - wf)
+        np.testing.assert_array_equal(o[:rf], y_batch[:rf])
+        wf = wf_new
+        prev = o
+    np.testing.assert_array_equal(out.cpu().numpy(), y_batch)
+
+
+def test_stream_argument_checks():
+    from packed_windowed_attention_amd import aut
+    torch = torch_mod()
+    cfg_d = small_cfg("fp32")
+    cfg, packed = pack(cfg_d, si.params(cfg_d, seed=1))
+    fbuf = torch.zeros((128, 1000), dtype=torch.float32, device="cuda")
+    out = torch.zeros((200, cfg_d["output_dim"]), dtype=torch.float32, device="cuda")
+    ws = aut.stream_workspace(cfg, 1000, "fp32")
+    for frames, wf in ((1200, 0), (900, 2)):   # more frames than T_max; windows not complete
+        with pytest.raises(RuntimeError) as e:
+            aut.encode_stream(cfg, fbuf, frames, wf, packed, "fp32", out, ws)
+        assert "AUT_ERR_INVALID_ARG" in str(e.value)
+    # nothing left to encode: no launch, no error
+    assert aut.encode_stream(cfg, fbuf, 800, 1, packed, "fp32", out, ws) == 1

@@ -274,6 +274,22 @@ def test_window_isolation_bitwise():
     assert changed == [1]
 
 
+def test_stream_suffix_equals_batch():
+    """Windows are independent (m-star module summary; openarchlab "1A",
+    section 4), so encoding a request's frames from a window boundary on gives
+    exactly its rows from that window's first row on: the basis of the
+    incremental encode."""
+    cfg = small_cfg()
+    L = 1850
+    feats = si.mel_features(np.array([L]), seed=9)
+    P = si.params(cfg, seed=9, std=0.05)
+    y, _ = ao.forward(feats, np.array([L]), P, cfg)
+    for wf in (1, 2):
+        sub = np.ascontiguousarray(feats[:, :, 800 * wf:])
+        ys, _ = ao.forward(sub, np.array([L - 800 * wf]), P, cfg)
+        np.testing.assert_array_equal(ys, y[104 * wf:])
+
+
 def test_request_permutation():
     cfg = small_cfg(encoder_layers=1)
     lens = np.array([250, 800, 37])
