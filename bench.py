@@ -127,6 +127,30 @@ def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_mib,
     print("\n".join(out))
 
 
+def inject_rate(aut, torch, out, reps=20):
+    """The step after the encoder: the batch's [T, 2048] fp32 output rows into
+    a bf16 decoder sequence of T + 512 rows at placeholder positions
+    (aut_inject_audio). Algorithmic bytes: fp32 rows read, bf16 rows written,
+    row indices read."""
+    T, D = out.shape
+    S = T + 512
+    rng = np.random.default_rng(3)
+    rows = torch.from_numpy(np.sort(rng.choice(S, size=T, replace=False)).astype(np.int32)).cuda()
+    dst = torch.zeros((S, D), dtype=torch.bfloat16, device="cuda")
+    aut.inject_audio(out, rows, dst, "bf16")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        aut.inject_audio(out, rows, dst, "bf16")
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / reps
+    nbytes = T * D * 4 + T * D * 2 + T * 4
+    return {"rows": int(T), "dim": int(D), "us": us, "gbs": nbytes / (us * 1e-6) / 1e9,
+            "peak_gbs": PEAK_HBM_GBS, "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+
+
 def stream_latency(aut, torch, cfg, packed, dtype, feats, steps, append=100):
     """Incremental encode of one live request (the workload's first request's
     mel, repeated as needed) receiving `append` frames per step: each step
@@ -340,6 +364,8 @@ def main():
         allf = sum(s["flops"] for c, s in stats.items() if c != "layernorm")
         res["mfma_frac_step"] = allf / args.steps / (ms_per_step / 1e3) / 1e12 / peak
         res["attention_gbs"] = a["bytes"] / (a["total_ms"] / 1e3) / 1e9 if a["total_ms"] else None
+    res["inject"] = inject_rate(aut, torch, out)
+    log(f"inject: {res['inject']['us']:.1f} us, {res['inject']['gbs']:.0f} GB/s")
     if args.stream_steps > 0:
         res["stream"] = stream_latency(aut, torch, cfg, packed, dtype, feats, args.stream_steps)
         log(f"stream: {res['stream']['step_ms_p50']:.3f} ms per 1 s append (p50)")

@@ -251,6 +251,28 @@ aut_status aut_encode_stream(const aut_config* cfg, const float* features, int32
                              aut_dtype dtype, float* out, void* workspace, size_t workspace_bytes,
                              void* stream, int32_t* windows_final_after);
 
+/* ------------------------------------------------------------------------
+ * After the encoder: audio rows into the decoder's embedding sequence
+ * ("Audio Encoder Component", cubic.dev wiki, Data Flow and Integration: the
+ * audio features are placed at the <|audio_pad|> placeholder positions of the
+ * text sequence, not appended).
+ * ------------------------------------------------------------------------ */
+
+/* Host only: the positions of the n_ids-long token sequence `ids` (host) that
+ * hold pad_id, in order, into rows (host, n_audio entries).  The count must
+ * equal n_audio (one placeholder per audio row), else AUT_ERR_INVALID_ARG. */
+aut_status aut_audio_rows(const int32_t* ids, int64_t n_ids, int32_t pad_id, int64_t n_audio,
+                          int32_t* rows);
+
+/* dst[rows[j]] = audio[j] for j < n_audio: audio device fp32 [n_audio, dim]
+ * (e.g. one request's rows of the encoder output), rows device int32
+ * [n_audio] (from aut_audio_rows), dst device [dst_rows, dim] of dst_dtype
+ * (fp32 copy, or bf16 rounded to nearest even); other rows of dst are not
+ * touched, and entries of rows outside [0, dst_rows) are skipped.  dim must be
+ * a multiple of 4 and audio/dst 16-byte aligned.  Asynchronous on `stream`. */
+aut_status aut_inject_audio(const float* audio, const int32_t* rows, int64_t n_audio, int32_t dim,
+                            void* dst, int64_t dst_rows, aut_dtype dst_dtype, void* stream);
+
 /* Kernel classes for the optional per-launch timing below. */
 typedef enum {
   AUT_K_CONV1 = 0,     /* conv1 (+GELU), fp32 vector ALU */

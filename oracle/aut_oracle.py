@@ -328,3 +328,42 @@ def forward_windows(features, feature_lens, P: dict, cfg: dict, windows):
         n = hidden.shape[0]
         res[w] = (pl["cu_seqlens"][w], encode(hidden, [0, n], P, cfg))
     return res
+
+
+# ---------------------------------------------------------------------------
+# after the encoder: audio rows into the decoder's embedding sequence
+# ---------------------------------------------------------------------------
+
+
+def audio_rows(ids, pad_id: int, n_audio: int) -> np.ndarray:
+    """Positions of the <|audio_pad|> placeholders in a token-id sequence, in
+    order ("Audio Encoder Component", cubic.dev wiki, Data Flow and Integration:
+    the audio features go into the text sequence at the placeholder positions,
+    not appended).  There must be exactly one placeholder per audio row."""
+    ids = np.asarray(ids)
+    pos = np.nonzero(ids == pad_id)[0]
+    if len(pos) != n_audio:
+        raise ValueError(f"{len(pos)} placeholders for {n_audio} audio rows")
+    return pos
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float64/float32 -> the nearest bfloat16 value (ties to even), as float32:
+    keep the top 16 bits of the float32 pattern after adding the rounding bias
+    0x7FFF plus the lowest kept bit (NaN inputs are not expected here)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def inject_audio(embeds: np.ndarray, ids, pad_id: int, audio: np.ndarray, out_dtype="fp32"):
+    """The decoder's input sequence: row i is the text embedding `embeds[i]`
+    unless ids[i] is the placeholder, in which case it is the next audio row
+    (same passage as ``audio_rows``).  out_dtype "bf16": every row stored as
+    bfloat16 (round to nearest even), the text rows being bf16 already."""
+    pos = audio_rows(ids, pad_id, audio.shape[0])
+    out = np.array(embeds, dtype=np.float64, copy=True)
+    out[pos] = audio
+    if out_dtype == "bf16":
+        out = bf16_round(out).astype(np.float64)
+    return out

@@ -75,6 +75,9 @@ SIGNATURES = {
     "aut_stream_workspace_bytes": (c_int, [POINTER(AutConfig), c_int32, c_int, POINTER(c_size_t)]),
     "aut_encode_stream": (c_int, [POINTER(AutConfig), c_void_p, c_int32, c_int32, c_int32, c_void_p,
                                   c_int, c_void_p, c_void_p, c_size_t, c_void_p, POINTER(c_int32)]),
+    "aut_audio_rows": (c_int, [POINTER(c_int32), c_int64, c_int32, c_int64, POINTER(c_int32)]),
+    "aut_inject_audio": (c_int, [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_int64, c_int,
+                                 c_void_p]),
     "aut_profile_enable": (c_int, [c_int]),
     "aut_profile_collect": (c_int, [POINTER(AutKernelStats)]),
     "aut_last_error": (c_char_p, []),
@@ -315,6 +318,24 @@ def encode_stream(cfg: AutConfig, features, frames_total: int, windows_final: in
                                    int(windows_final), _ptr(packed), _dtype(dtype), _ptr(out),
                                    _ptr(ws), ws.numel(), _stream_ptr(stream), byref(after)))
     return after.value
+
+
+def audio_rows(ids, pad_id: int, n_audio: int) -> list:
+    """aut_audio_rows: placeholder positions of a token-id sequence (host)."""
+    ids = [int(x) for x in ids]
+    arr = (c_int32 * max(1, len(ids)))(*ids)
+    rows = (c_int32 * max(1, int(n_audio)))()
+    _check(lib().aut_audio_rows(arr, len(ids), int(pad_id), int(n_audio), rows))
+    return list(rows)[:int(n_audio)]
+
+
+def inject_audio(audio, rows, dst, dst_dtype, stream=None):
+    """aut_inject_audio: dst[rows[j]] = audio[j] on the device (rows: int32 device tensor)."""
+    if str(rows.dtype) != "torch.int32":
+        raise TypeError("rows must be int32")
+    _check(lib().aut_inject_audio(_ptr(audio), _ptr(rows), rows.numel(), audio.shape[1], _ptr(dst),
+                                  dst.shape[0], _dtype(dst_dtype), _stream_ptr(stream)))
+    return dst
 
 
 def profile_enable(on: bool):

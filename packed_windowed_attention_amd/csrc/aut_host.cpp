@@ -866,6 +866,44 @@ extern "C" aut_status aut_encode_stream(const aut_config* cfg, const float* feat
 }
 
 // ---------------------------------------------------------------------------
+// audio rows into the decoder sequence
+// ---------------------------------------------------------------------------
+
+extern "C" aut_status aut_audio_rows(const int32_t* ids, int64_t n_ids, int32_t pad_id,
+                                     int64_t n_audio, int32_t* rows) {
+  if (n_ids < 0 || n_audio < 0) return fail(AUT_ERR_INVALID_ARG, "negative length");
+  if (n_ids > 0 && !ids) return fail(AUT_ERR_INVALID_ARG, "ids is NULL");
+  if (n_audio > 0 && !rows) return fail(AUT_ERR_INVALID_ARG, "rows is NULL");
+  if (n_ids > INT32_MAX) return fail(AUT_ERR_UNSUPPORTED, "sequence longer than 2^31 - 1");
+  int64_t k = 0;
+  for (int64_t i = 0; i < n_ids; ++i)
+    if (ids[i] == pad_id) {
+      if (k < n_audio) rows[k] = (int32_t)i;
+      ++k;
+    }
+  if (k != n_audio)
+    return fail(AUT_ERR_INVALID_ARG, "%lld placeholders for %lld audio rows", (long long)k,
+                (long long)n_audio);
+  return AUT_OK;
+}
+
+extern "C" aut_status aut_inject_audio(const float* audio, const int32_t* rows, int64_t n_audio,
+                                       int32_t dim, void* dst, int64_t dst_rows,
+                                       aut_dtype dst_dtype, void* stream) {
+  if (n_audio < 0 || dst_rows < 0) return fail(AUT_ERR_INVALID_ARG, "negative length");
+  if (dst_dtype != AUT_FP32 && dst_dtype != AUT_BF16) return fail(AUT_ERR_INVALID_ARG, "bad dtype");
+  if (n_audio == 0) return AUT_OK;
+  if (!audio || !rows || !dst) return fail(AUT_ERR_INVALID_ARG, "NULL buffer");
+  if (dim <= 0 || dim % 4) return fail(AUT_ERR_INVALID_ARG, "dim = %d must be a positive multiple of 4", dim);
+  if (((size_t)audio & 15) || ((size_t)dst & 15))
+    return fail(AUT_ERR_INVALID_ARG, "audio and dst must be 16-byte aligned");
+  hipError_t e = aut::launch_inject(audio, rows, (long)n_audio, dim, dst, (long)dst_rows, dst_dtype,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AUT_ERR_HIP, "inject launch failed: %s", hipGetErrorString(e));
+  return AUT_OK;
+}
+
+// ---------------------------------------------------------------------------
 // timing and errors
 // ---------------------------------------------------------------------------
 

@@ -25,6 +25,10 @@ struct Geometry {
 
 Geometry geometry(const aut_config& c);
 
+// Audio rows into a decoder embedding sequence: dst[rows[j]] = audio[j].
+hipError_t launch_inject(const float* audio, const int* rows, long n, int dim, void* dst,
+                         long dst_rows, aut_dtype dt, hipStream_t s);
+
 // Per-launch timing hooks (no-ops unless aut_profile_enable(1)).
 void prof_begin(hipStream_t s);
 void prof_end(hipStream_t s, aut_kernel_class cls, double flops, double bytes);

@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = aut.lib()
     names = declared_functions()
-    assert len(names) == len(aut.SIGNATURES) == 20
+    assert len(names) == len(aut.SIGNATURES) == 22
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(aut.SIGNATURES), "binding and header disagree"
@@ -199,3 +199,28 @@ def test_stream_workspace_covers_each_step():
         assert lib.aut_stream_workspace_bytes(ct.byref(cfg), mx, aut.DTYPES["bf16"], ct.byref(n)) == 0
         for L in (1, mx // 3, mx):
             assert aut.workspace_bytes(cfg, aut.plan(cfg, [L]), "bf16") <= n.value
+
+
+def test_audio_rows_vs_oracle():
+    """aut_audio_rows (host) against the oracle's placeholder positions."""
+    rng = np.random.default_rng(17)
+    PAD = 151676
+    for n in (0, 1, 5, 300, 4000):
+        ids = rng.integers(0, 150000, size=n + 37).astype(np.int32)
+        pos = np.sort(rng.choice(n + 37, size=n, replace=False))
+        ids[pos] = PAD
+        assert aut.audio_rows(ids, PAD, n) == [int(x) for x in oracle.audio_rows(ids, PAD, n)]
+    with pytest.raises(RuntimeError) as e:
+        aut.audio_rows([1, PAD, 2], PAD, 2)
+    assert "AUT_ERR_INVALID_ARG" in str(e.value)
+
+
+def test_inject_argument_checks_before_launch():
+    lib = aut.lib()
+    import ctypes as ct
+    ok_ptr = ct.c_void_p(16)
+    assert lib.aut_inject_audio(None, None, 0, 2048, None, 0, 0, None) == 0      # nothing to do
+    assert lib.aut_inject_audio(None, ok_ptr, 4, 2048, ok_ptr, 10, 0, None) == 1  # NULL audio
+    assert lib.aut_inject_audio(ok_ptr, ok_ptr, 4, 2046, ok_ptr, 10, 0, None) == 1  # dim % 4
+    assert lib.aut_inject_audio(ok_ptr, ok_ptr, -1, 2048, ok_ptr, 10, 0, None) == 1
+    assert lib.aut_inject_audio(ok_ptr, ok_ptr, 4, 2048, ok_ptr, 10, 7, None) == 1  # dtype

@@ -376,3 +376,37 @@ def test_planted_mistakes(name, monkeypatch):
     monkeypatch.setattr(ao, attr, make(orig))
     err = check()
     assert err > 1e-6, f"pin did not catch: {name} (err={err})"
+
+
+# ---------------------------------------------------------------------------
+# audio rows into the decoder sequence
+# ---------------------------------------------------------------------------
+
+
+def test_inject_audio_worked_example():
+    """Placeholders take the audio rows in order; other rows keep their text
+    embedding; the count must match."""
+    PAD = 151676
+    ids = [9, PAD, 4, PAD, PAD, 7]
+    emb = np.arange(6 * 3, dtype=np.float64).reshape(6, 3)
+    aud = -np.arange(1, 10, dtype=np.float64).reshape(3, 3)
+    out = ao.inject_audio(emb, ids, PAD, aud)
+    expect = np.array([[0, 1, 2], [-1, -2, -3], [6, 7, 8], [-4, -5, -6], [-7, -8, -9], [15, 16, 17]],
+                      dtype=np.float64)
+    np.testing.assert_array_equal(out, expect)
+    np.testing.assert_array_equal(ao.audio_rows(ids, PAD, 3), [1, 3, 4])
+    with pytest.raises(ValueError):
+        ao.audio_rows(ids, PAD, 2)
+    with pytest.raises(ValueError):
+        ao.inject_audio(emb, ids, PAD, aud[:2])
+
+
+def test_bf16_round_vs_torch():
+    """Round-to-nearest-even to bfloat16 against torch's conversion, including
+    ties and values at the edges of the exponent range."""
+    torch = pytest.importorskip("torch")
+    x = np.concatenate([RNG.normal(size=4000) * 10.0 ** RNG.integers(-30, 30, 4000),
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 3.0e38, 1e-40, 0.0])])
+    x32 = x.astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(ao.bf16_round(x32), ref)
