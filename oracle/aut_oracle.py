@@ -367,3 +367,83 @@ def inject_audio(embeds: np.ndarray, ids, pad_id: int, audio: np.ndarray, out_dt
     if out_dtype == "bf16":
         out = bf16_round(out).astype(np.float64)
     return out
+
+
+# ---------------------------------------------------------------------------
+# before the encoder: Whisper-style log-mel of 16 kHz mono audio
+# ---------------------------------------------------------------------------
+# The pages fix 16 kHz mono input, 128 mel bins and 100 frames per second
+# ("Audio Encoder Component", cubic.dev wiki, Processing Pipeline; m-star
+# module summary: a Whisper-style log-mel input).  Everything else is the
+# published Whisper front end, taken as the reading: a 400-sample periodic
+# Hann window and 400-point DFT every 160 samples, frames centred by reflect
+# padding of 200 samples, the last frame dropped (N // 160 frames); the power
+# spectrum; a Slaney-scale, Slaney-normalised triangular mel filterbank over
+# 0..8000 Hz; log10 of max(mel, 1e-10); a floor at (the request's maximum - 8);
+# then (x + 4) / 4.
+
+SAMPLE_RATE = 16000
+N_FFT = 400
+HOP = 160
+
+
+def hz_to_mel(f):
+    """Slaney mel scale: linear 3/200 mel per Hz below 1 kHz (15 mel at 1 kHz),
+    logarithmic above, 27 mel per factor 6.4."""
+    f = np.asarray(f, dtype=np.float64)
+    lin = 3.0 * f / 200.0
+    log = 15.0 + 27.0 * np.log(np.maximum(f, 1e-300) / 1000.0) / np.log(6.4)
+    return np.where(f >= 1000.0, log, lin)
+
+
+def mel_to_hz(m):
+    m = np.asarray(m, dtype=np.float64)
+    return np.where(m >= 15.0, 1000.0 * np.exp((m - 15.0) * np.log(6.4) / 27.0), 200.0 * m / 3.0)
+
+
+def mel_filterbank(n_mels: int = 128) -> np.ndarray:
+    """[n_mels, N_FFT // 2 + 1] triangles between n_mels + 2 points equally spaced
+    in mel from 0 Hz to the Nyquist frequency, each scaled to unit area
+    (2 / (upper edge - lower edge))."""
+    freqs = np.linspace(0.0, SAMPLE_RATE / 2.0, N_FFT // 2 + 1)
+    pts = mel_to_hz(np.linspace(0.0, float(hz_to_mel(SAMPLE_RATE / 2.0)), n_mels + 2))
+    w = np.zeros((n_mels, freqs.size))
+    for m in range(n_mels):
+        lo, c, hi = pts[m], pts[m + 1], pts[m + 2]
+        rise = (freqs - lo) / (c - lo)
+        fall = (hi - freqs) / (hi - c)
+        w[m] = np.maximum(0.0, np.minimum(rise, fall)) * (2.0 / (hi - lo))
+    return w
+
+
+def hann(n: int = N_FFT) -> np.ndarray:
+    """Periodic Hann window (the DFT-even form)."""
+    return 0.5 - 0.5 * np.cos(2.0 * np.pi * np.arange(n) / n)
+
+
+def frames_for_samples(n_samples: int) -> int:
+    return int(n_samples) // HOP
+
+
+def power_spectrum(audio) -> np.ndarray:
+    """[N // HOP, N_FFT // 2 + 1] |DFT|^2 of the windowed, centred frames."""
+    x = np.asarray(audio, dtype=np.float64)
+    nf = frames_for_samples(x.size)
+    if nf == 0:
+        return np.zeros((0, N_FFT // 2 + 1))
+    if x.size <= N_FFT // 2:
+        raise ValueError("reflect padding needs more than N_FFT / 2 samples")
+    xp = np.pad(x, N_FFT // 2, mode="reflect")
+    fr = np.stack([xp[f * HOP:f * HOP + N_FFT] for f in range(nf)]) * hann()
+    return np.abs(np.fft.rfft(fr, axis=1)) ** 2
+
+
+def log_mel(audio, n_mels: int = 128) -> np.ndarray:
+    """[n_mels, N // HOP] Whisper-style log-mel of one request."""
+    p = power_spectrum(audio)
+    if p.shape[0] == 0:
+        return np.zeros((n_mels, 0))
+    mel = mel_filterbank(n_mels) @ p.T
+    lg = np.log10(np.maximum(mel, 1e-10))
+    lg = np.maximum(lg, lg.max() - 8.0)
+    return (lg + 4.0) / 4.0

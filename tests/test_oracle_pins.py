@@ -318,6 +318,50 @@ def test_forward_windows_exact():
 # planted mistakes: each must make its pin fail
 
 
+def check_power():
+    import torch
+    x = np.random.default_rng(41).normal(size=7 * 160 + 91)
+    ref = torch.stft(torch.from_numpy(x), 400, 160, window=torch.hann_window(400, dtype=torch.float64),
+                     center=True, pad_mode="reflect", return_complex=True)
+    ref = (ref.abs() ** 2)[:, :-1].numpy().T
+    got = ao.power_spectrum(x)
+    if got.shape != ref.shape:
+        return float("inf")
+    return float(np.abs(got - ref).max() / np.abs(ref).max())
+
+
+def check_mel_scale():
+    e1 = np.abs(ao.hz_to_mel(np.array([0.0, 500.0, 1000.0, 6400.0])) - np.array([0.0, 7.5, 15.0, 42.0])).max()
+    f = np.linspace(0, 8000, 321)
+    e2 = np.abs(ao.mel_to_hz(ao.hz_to_mel(f)) - f).max()
+    return float(max(e1, e2))
+
+
+def check_fbank():
+    w = ao.mel_filterbank(128)
+    pts = ao.mel_to_hz(np.linspace(0.0, float(ao.hz_to_mel(8000.0)), 130))
+    freqs = np.linspace(0, 8000, 201)
+    tri = w * ((pts[2:] - pts[:-2]) / 2.0)[:, None]
+    inside = (freqs >= pts[1]) & (freqs <= pts[128])
+    return float(np.abs(tri.sum(axis=0)[inside] - 1.0).max())
+
+
+def check_log_mel():
+    import torch
+    rng = np.random.default_rng(43)
+    # a loud part and silence: a dynamic range well over the floor's 8 decades
+    x = np.concatenate([rng.normal(size=3200) * 1000.0, np.zeros(1600)])
+    spec = torch.stft(torch.from_numpy(x), 400, 160, window=torch.hann_window(400, dtype=torch.float64),
+                      center=True, pad_mode="reflect", return_complex=True)[:, :-1]
+    mel = torch.from_numpy(ao.mel_filterbank(128)) @ (spec.abs() ** 2)
+    lg = torch.clamp(mel, min=1e-10).log10()
+    lg = torch.maximum(lg, lg.max() - 8.0)
+    ref = ((lg + 4.0) / 4.0).numpy()
+    got = ao.log_mel(x)
+    e = float(np.abs(got - ref).max()) if got.shape == ref.shape else float("inf")
+    return max(e, abs(ao.frames_for_samples(16000) - 100) * 1.0)
+
+
 MUTATIONS = {
     "conv kernel transposed": ("conv2d_k3s2p1", lambda orig: (lambda x, w, b: orig(x, np.swapaxes(w, 2, 3), b)), check_conv),
     "conv bias dropped": ("conv2d_k3s2p1", lambda orig: (lambda x, w, b: orig(x, w, np.zeros_like(b))), check_conv),
@@ -334,7 +378,28 @@ MUTATIONS = {
     "post-LN layer order": ("encoder_layer", lambda orig: _post_ln_layer, check_composition),
     "qkv split k/v swapped": ("window_attention", lambda orig: (lambda q, k, v, cu, H: orig(q, v, k, cu, H)), check_composition),
     "positions not chunk-local": ("sinusoid_table", lambda orig: (lambda n, c: orig(n + 1, c)[1:]), check_composition),
+    "magnitude instead of power": ("power_spectrum", lambda orig: (lambda a: np.sqrt(orig(a))), check_power),
+    "symmetric Hann": ("hann", lambda orig: (lambda n=400: 0.5 - 0.5 * np.cos(2 * np.pi * np.arange(n) / (n - 1))), check_power),
+    "HTK mel scale": ("hz_to_mel", lambda orig: (lambda f: 2595.0 * np.log10(1.0 + np.asarray(f, dtype=np.float64) / 700.0)), check_mel_scale),
+    "filterbank not unit area": ("mel_filterbank", lambda orig: (lambda n=128: orig(n) / orig(n).max(axis=1, keepdims=True)), check_fbank),
+    "last frame kept": ("frames_for_samples", lambda orig: (lambda n: int(n) // 160 + 1), check_log_mel),
+    "natural log": ("log_mel", lambda orig: _log_mel_ln, check_log_mel),
+    "floor at max - 10": ("log_mel", lambda orig: _log_mel_floor10, check_log_mel),
 }
+
+
+def _log_mel_ln(audio, n_mels=128):
+    p = ao.power_spectrum(audio)
+    lg = np.log(np.maximum(ao.mel_filterbank(n_mels) @ p.T, 1e-10))
+    lg = np.maximum(lg, lg.max() - 8.0)
+    return (lg + 4.0) / 4.0
+
+
+def _log_mel_floor10(audio, n_mels=128):
+    p = ao.power_spectrum(audio)
+    lg = np.log10(np.maximum(ao.mel_filterbank(n_mels) @ p.T, 1e-10))
+    lg = np.maximum(lg, lg.max() - 10.0)
+    return (lg + 4.0) / 4.0
 
 
 def _causal_attn(q, k, v, cu, H):
@@ -410,3 +475,86 @@ def test_bf16_round_vs_torch():
     x32 = x.astype(np.float32)
     ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float32).numpy()
     np.testing.assert_array_equal(ao.bf16_round(x32), ref)
+
+
+# ---------------------------------------------------------------------------
+# log-mel front end
+# ---------------------------------------------------------------------------
+
+
+def test_log_mel_page_rates():
+    """16 kHz mono in, 100 frames per second, 128 bins out (cubic.dev wiki,
+    Processing Pipeline; m-star module summary)."""
+    x = RNG.normal(size=16000)
+    assert ao.frames_for_samples(16000) == 100
+    assert ao.log_mel(x).shape == (128, 100)
+    assert ao.power_spectrum(RNG.normal(size=800 * 160 + 37)).shape == (800, 201)
+
+
+def test_mel_scale_special_points():
+    """Slaney scale: 0 Hz -> 0, 1 kHz -> 15 mel (end of the linear part),
+    6.4 kHz -> 42 mel (one factor 6.4 above 1 kHz = 27 mel), and round trips."""
+    np.testing.assert_allclose(ao.hz_to_mel([0.0, 1000.0, 6400.0]), [0.0, 15.0, 42.0], atol=1e-12)
+    np.testing.assert_allclose(ao.hz_to_mel(500.0), 7.5, atol=1e-12)
+    f = np.linspace(0, 8000, 321)
+    np.testing.assert_allclose(ao.mel_to_hz(ao.hz_to_mel(f)), f, atol=1e-9)
+
+
+def test_mel_filterbank_structure():
+    """Triangles with unit area: scaled back by (upper - lower) / 2 they form a
+    partition of unity between the first and last centre frequency, each
+    non-zero only between its neighbours' centres, peaking at its own."""
+    w = ao.mel_filterbank(128)
+    assert w.shape == (128, 201) and (w >= 0).all()
+    pts = ao.mel_to_hz(np.linspace(0.0, float(ao.hz_to_mel(8000.0)), 130))
+    freqs = np.linspace(0, 8000, 201)
+    tri = w * ((pts[2:] - pts[:-2]) / 2.0)[:, None]
+    inside = (freqs >= pts[1]) & (freqs <= pts[128])
+    np.testing.assert_allclose(tri.sum(axis=0)[inside], 1.0, atol=1e-12)
+    for m in range(128):
+        nz = np.nonzero(w[m])[0]
+        if nz.size:
+            assert freqs[nz].min() > pts[m] - 1e-9 and freqs[nz].max() < pts[m + 2] + 1e-9
+            assert abs(freqs[nz[np.argmax(w[m, nz])]] - pts[m + 1]) <= 20.0 + 1e-9
+
+
+def test_power_spectrum_vs_torch_stft():
+    """Framing, window and DFT against torch.stft (centred, reflect padding,
+    periodic Hann, last frame dropped)."""
+    torch = pytest.importorskip("torch")
+    x = RNG.normal(size=7 * 160 + 91)
+    ref = torch.stft(torch.from_numpy(x), 400, 160, window=torch.hann_window(400, dtype=torch.float64),
+                     center=True, pad_mode="reflect", return_complex=True)
+    ref = (ref.abs() ** 2)[:, :-1].numpy().T
+    np.testing.assert_allclose(ao.power_spectrum(x), ref, rtol=1e-10, atol=1e-9)
+
+
+def test_power_spectrum_pure_tone():
+    """A cosine on DFT bin k: in every frame away from the edges the power sits
+    in bins k-1, k, k+1 with the Hann window's closed-form weights
+    (N/4 * A)^2 and (N/8 * A)^2."""
+    A, k = 0.3, 25
+    n = np.arange(50 * 160)
+    x = A * np.cos(2 * np.pi * k * n / 400)
+    p = ao.power_spectrum(x)[5:-5]
+    np.testing.assert_allclose(p[:, k], (400 / 4 * A) ** 2, rtol=1e-9)
+    np.testing.assert_allclose(p[:, k - 1], (400 / 8 * A) ** 2, rtol=1e-9)
+    np.testing.assert_allclose(p[:, k + 1], (400 / 8 * A) ** 2, rtol=1e-9)
+    rest = np.delete(p, [k - 1, k, k + 1], axis=1)
+    assert rest.max() < 1e-18 * p[:, k].max() + 1e-20
+
+
+def test_log_mel_floor_and_scale():
+    """Silence: every value log10(1e-10) = -10 -> (-10 + 4) / 4 = -1.5; the floor
+    keeps the dynamic range to 8 (in log10 units, 2 after the scaling)."""
+    np.testing.assert_array_equal(ao.log_mel(np.zeros(3200)), np.full((128, 20), -1.5))
+    y = ao.log_mel(RNG.normal(size=32000) * np.exp(RNG.normal(size=32000) * 3))
+    assert y.max() - y.min() <= 2.0 + 1e-12
+    torch = pytest.importorskip("torch")
+    x = RNG.normal(size=4800)
+    spec = torch.stft(torch.from_numpy(x), 400, 160, window=torch.hann_window(400, dtype=torch.float64),
+                      center=True, pad_mode="reflect", return_complex=True)[:, :-1]
+    mel = torch.from_numpy(ao.mel_filterbank(128)) @ (spec.abs() ** 2)
+    lg = torch.clamp(mel, min=1e-10).log10()
+    lg = torch.maximum(lg, lg.max() - 8.0)
+    np.testing.assert_allclose(ao.log_mel(x), ((lg + 4.0) / 4.0).numpy(), rtol=1e-12, atol=1e-12)
