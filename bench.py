@@ -127,6 +127,33 @@ def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_mib,
     print("\n".join(out))
 
 
+def logmel_rate(aut, torch, frame_lens, reps=10):
+    """The step before the encoder: the same batch's audio (16 kHz, 160 samples
+    per frame; seeded speech-like stand-in) to log-mel on the GPU
+    (aut_logmel). Algorithmic flops: the windowed DFT as a [frames x 400] x
+    [400 x 416] product plus the [frames x 208] x [208 x 128] filterbank, fp32
+    on the matrix cores (peak 157.3 TFLOP/s)."""
+    n = np.asarray(frame_lens, dtype=np.int64) * 160
+    audio = torch.from_numpy(si.audio_samples(n, seed=8)).cuda()
+    tables = aut.logmel_tables()
+    T_max = (int(max(n)) // 160 + 3) // 4 * 4
+    feats = torch.empty((len(n), 128, T_max), dtype=torch.float32, device="cuda")
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    aut.logmel(audio, n, tables, feats, ws=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        aut.logmel(audio, n, tables, feats, ws=ws)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / reps
+    frames = float(np.sum(n // 160))
+    flops = frames * (2.0 * 400 * 416 + 2.0 * 208 * 128)
+    return {"frames": int(frames), "audio_seconds": frames / 100.0, "ms": ms,
+            "audio_s_per_s": frames / 100.0 / (ms * 1e-3), "tflops": flops / (ms * 1e-3) / 1e12,
+            "peak_tflops": PEAK_FP32_TFLOPS, "frac": flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+            "note": "wall time per call incl. the length upload and one stream sync"}
+
+
 def inject_rate(aut, torch, out, reps=20):
     """The step after the encoder: the batch's [T, 2048] fp32 output rows into
     a bf16 decoder sequence of T + 512 rows at placeholder positions
@@ -364,6 +391,8 @@ def main():
         allf = sum(s["flops"] for c, s in stats.items() if c != "layernorm")
         res["mfma_frac_step"] = allf / args.steps / (ms_per_step / 1e3) / 1e12 / peak
         res["attention_gbs"] = a["bytes"] / (a["total_ms"] / 1e3) / 1e9 if a["total_ms"] else None
+    res["logmel"] = logmel_rate(aut, torch, lens)
+    log(f"logmel: {res['logmel']['ms']:.3f} ms for {res['logmel']['audio_seconds']:.0f} s of audio")
     res["inject"] = inject_rate(aut, torch, out)
     log(f"inject: {res['inject']['us']:.1f} us, {res['inject']['gbs']:.0f} GB/s")
     if args.stream_steps > 0:

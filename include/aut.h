@@ -252,6 +252,36 @@ aut_status aut_encode_stream(const aut_config* cfg, const float* features, int32
                              void* stream, int32_t* windows_final_after);
 
 /* ------------------------------------------------------------------------
+ * Before the encoder: Whisper-style log-mel of 16 kHz mono audio
+ * ("Audio Encoder Component", cubic.dev wiki, Processing Pipeline: 16 kHz
+ * mono audio becomes a 128-bin mel spectrogram; m-star module summary: a
+ * Whisper-style log-mel input at 100 frames/s).  Beyond what the pages fix,
+ * the published Whisper front end: 400-sample periodic Hann window and
+ * 400-point DFT every 160 samples on reflect-padded centred frames
+ * (sample_len / 160 frames), power spectrum, Slaney mel filterbank over
+ * 0..8000 Hz, log10 of max(mel, 1e-10), floor at the request's maximum - 8,
+ * then (x + 4) / 4.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of the constant tables (window x DFT, mel filterbank), and filling
+ * them on the device (once; caller-owned device buffer, 256-byte aligned). */
+aut_status aut_logmel_tables_bytes(size_t* bytes);
+aut_status aut_logmel_tables_init(void* tables, size_t bytes, void* stream);
+
+/* Workspace bytes for B requests. */
+aut_status aut_logmel_workspace_bytes(int32_t B, size_t* bytes);
+
+/* audio: device fp32 [B, S_max] (request b's samples first, sample_lens[b] of
+ * them, host int32, each 0 or > 200 and <= S_max); features: device fp32
+ * [B, 128, T_max], T_max >= max(sample_lens) / 160 and a multiple of 4 for the
+ * 16-byte stores; frames past a request's count are not written.  Copies the
+ * lengths into the workspace and synchronises the stream once, like
+ * aut_encode; the rest is asynchronous. */
+aut_status aut_logmel(const float* audio, int32_t S_max, const int32_t* sample_lens, int32_t B,
+                      const void* tables, float* features, int32_t T_max, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * After the encoder: audio rows into the decoder's embedding sequence
  * ("Audio Encoder Component", cubic.dev wiki, Data Flow and Integration: the
  * audio features are placed at the <|audio_pad|> placeholder positions of the
@@ -281,7 +311,8 @@ typedef enum {
   AUT_K_LAYERNORM = 3, /* LayerNorm rows -> GEMM operand */
   AUT_K_GEMM = 4,      /* qkv / out_proj / fc1 / fc2 / proj1 / proj2 */
   AUT_K_ATTENTION = 5, /* window attention */
-  AUT_K_COUNT = 6
+  AUT_K_LOGMEL = 6,    /* log-mel front end (DFT + filterbank + log, floor pass) */
+  AUT_K_COUNT = 7
 } aut_kernel_class;
 
 typedef struct {

@@ -17,7 +17,7 @@ AUT_OK = 0
 STATUS = {0: "AUT_OK", 1: "AUT_ERR_INVALID_ARG", 2: "AUT_ERR_UNSUPPORTED",
           3: "AUT_ERR_MISSING_WEIGHT", 4: "AUT_ERR_WORKSPACE_TOO_SMALL", 5: "AUT_ERR_HIP"}
 DTYPES = {"fp32": 0, "bf16": 1}
-KERNEL_CLASSES = ["conv1", "conv_gemm", "conv_out", "layernorm", "gemm", "attention"]
+KERNEL_CLASSES = ["conv1", "conv_gemm", "conv_out", "layernorm", "gemm", "attention", "logmel"]
 
 CONFIG_FIELDS = ["d_model", "encoder_layers", "encoder_attention_heads", "encoder_ffn_dim",
                  "num_mel_bins", "n_window", "n_window_infer", "conv_chunksize",
@@ -78,6 +78,11 @@ SIGNATURES = {
     "aut_audio_rows": (c_int, [POINTER(c_int32), c_int64, c_int32, c_int64, POINTER(c_int32)]),
     "aut_inject_audio": (c_int, [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_int64, c_int,
                                  c_void_p]),
+    "aut_logmel_tables_bytes": (c_int, [POINTER(c_size_t)]),
+    "aut_logmel_tables_init": (c_int, [c_void_p, c_size_t, c_void_p]),
+    "aut_logmel_workspace_bytes": (c_int, [c_int32, POINTER(c_size_t)]),
+    "aut_logmel": (c_int, [c_void_p, c_int32, POINTER(c_int32), c_int32, c_void_p, c_void_p, c_int32,
+                           c_void_p, c_size_t, c_void_p]),
     "aut_profile_enable": (c_int, [c_int]),
     "aut_profile_collect": (c_int, [POINTER(AutKernelStats)]),
     "aut_last_error": (c_char_p, []),
@@ -318,6 +323,37 @@ def encode_stream(cfg: AutConfig, features, frames_total: int, windows_final: in
                                    int(windows_final), _ptr(packed), _dtype(dtype), _ptr(out),
                                    _ptr(ws), ws.numel(), _stream_ptr(stream), byref(after)))
     return after.value
+
+
+def logmel_tables(device="cuda", stream=None):
+    """aut_logmel_tables_bytes + aut_logmel_tables_init: the constant tables on the device."""
+    import torch
+    n = c_size_t()
+    _check(lib().aut_logmel_tables_bytes(byref(n)))
+    t = torch.empty(n.value, dtype=torch.uint8, device=device)
+    _check(lib().aut_logmel_tables_init(_ptr(t), n.value, _stream_ptr(stream)))
+    return t
+
+
+def logmel(audio, sample_lens, tables, features=None, T_max=None, ws=None, stream=None):
+    """aut_logmel: audio fp32 [B, S_max] on the device -> features [B, 128, T_max]
+    (frames past a request's count are left as they are; a new buffer is zeroed)."""
+    import torch
+    lens = [int(x) for x in sample_lens]
+    B = len(lens)
+    if T_max is None:
+        T_max = max([n // 160 for n in lens] + [1])
+        T_max = (T_max + 3) // 4 * 4
+    if features is None:
+        features = torch.zeros((B, 128, T_max), dtype=torch.float32, device=audio.device)
+    if ws is None:
+        n = c_size_t()
+        _check(lib().aut_logmel_workspace_bytes(B, byref(n)))
+        ws = torch.empty(max(1, n.value), dtype=torch.uint8, device=audio.device)
+    arr = (c_int32 * max(1, B))(*lens)
+    _check(lib().aut_logmel(_ptr(audio), audio.shape[1], arr, B, _ptr(tables), _ptr(features),
+                            features.shape[2], _ptr(ws), ws.numel(), _stream_ptr(stream)))
+    return features
 
 
 def audio_rows(ids, pad_id: int, n_audio: int) -> list:

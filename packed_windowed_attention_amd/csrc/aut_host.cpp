@@ -866,6 +866,77 @@ extern "C" aut_status aut_encode_stream(const aut_config* cfg, const float* feat
 }
 
 // ---------------------------------------------------------------------------
+// log-mel front end
+// ---------------------------------------------------------------------------
+
+extern "C" aut_status aut_logmel_tables_bytes(size_t* bytes) {
+  if (!bytes) return fail(AUT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = aut::logmel_table_floats() * sizeof(float);
+  return AUT_OK;
+}
+
+extern "C" aut_status aut_logmel_tables_init(void* tables, size_t bytes, void* stream) {
+  if (!tables) return fail(AUT_ERR_INVALID_ARG, "tables is NULL");
+  if (bytes < aut::logmel_table_floats() * sizeof(float))
+    return fail(AUT_ERR_WORKSPACE_TOO_SMALL, "tables buffer has %zu bytes, needs %zu", bytes,
+                aut::logmel_table_floats() * sizeof(float));
+  if ((size_t)tables & 15) return fail(AUT_ERR_INVALID_ARG, "tables must be 16-byte aligned");
+  hipError_t e = aut::launch_logmel_tables((float*)tables, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AUT_ERR_HIP, "log-mel table launch failed: %s", hipGetErrorString(e));
+  return AUT_OK;
+}
+
+extern "C" aut_status aut_logmel_workspace_bytes(int32_t B, size_t* bytes) {
+  if (!bytes) return fail(AUT_ERR_INVALID_ARG, "bytes is NULL");
+  if (B < 0) return fail(AUT_ERR_INVALID_ARG, "B must be >= 0");
+  *bytes = align256((size_t)B * 4) + align256((size_t)B * 4);
+  return AUT_OK;
+}
+
+extern "C" aut_status aut_logmel(const float* audio, int32_t S_max, const int32_t* sample_lens,
+                                 int32_t B, const void* tables, float* features, int32_t T_max,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0) return fail(AUT_ERR_INVALID_ARG, "B must be >= 0");
+  if (B == 0) return AUT_OK;
+  if (!sample_lens) return fail(AUT_ERR_INVALID_ARG, "sample_lens is NULL");
+  int max_frames = 0;
+  for (int b = 0; b < B; ++b) {
+    const int n = sample_lens[b];
+    if (n < 0 || n > S_max)
+      return fail(AUT_ERR_INVALID_ARG, "sample_lens[%d] = %d outside [0, S_max = %d]", b, n, S_max);
+    if (n > 0 && n <= aut::LM_NFFT / 2)
+      return fail(AUT_ERR_INVALID_ARG, "sample_lens[%d] = %d: reflect padding needs more than %d samples",
+                  b, n, aut::LM_NFFT / 2);
+    max_frames = std::max(max_frames, n / aut::LM_HOP);
+  }
+  if (max_frames > T_max)
+    return fail(AUT_ERR_INVALID_ARG, "T_max = %d is below %d frames", T_max, max_frames);
+  if (T_max % 4) return fail(AUT_ERR_INVALID_ARG, "T_max must be a multiple of 4");
+  if (!audio || !tables || !features || !ws) return fail(AUT_ERR_INVALID_ARG, "NULL buffer");
+  if (((size_t)features & 15) || ((size_t)tables & 15))
+    return fail(AUT_ERR_INVALID_ARG, "features and tables must be 16-byte aligned");
+  size_t need = 0;
+  aut_logmel_workspace_bytes(B, &need);
+  if (ws_bytes < need) return fail(AUT_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  int* lens_dev = (int*)ws;
+  unsigned* mx = (unsigned*)((char*)ws + align256((size_t)B * 4));
+  hipError_t e = hipMemcpyAsync(lens_dev, sample_lens, (size_t)B * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // the host lengths may go away after the call
+  if (e != hipSuccess) return fail(AUT_ERR_HIP, "length upload failed: %s", hipGetErrorString(e));
+  aut::prof_begin(s);
+  e = aut::launch_logmel(audio, S_max, lens_dev, B, max_frames, (const float*)tables, features, T_max,
+                         mx, s);
+  if (e != hipSuccess) return fail(AUT_ERR_HIP, "log-mel launch failed: %s", hipGetErrorString(e));
+  double frames = 0;
+  for (int b = 0; b < B; ++b) frames += sample_lens[b] / aut::LM_HOP;
+  const int bins = 16 * aut::LM_BIN_TILES;
+  aut::prof_end(s, AUT_K_LOGMEL, frames * 2.0 * aut::LM_NFFT * 2 * bins + frames * 2.0 * bins * aut::LM_MELS,
+                frames * aut::LM_HOP * 4.0 + frames * aut::LM_MELS * 4.0 * 3);
+  return AUT_OK;
+}
+
+// ---------------------------------------------------------------------------
 // audio rows into the decoder sequence
 // ---------------------------------------------------------------------------
 

@@ -25,6 +25,17 @@ struct Geometry {
 
 Geometry geometry(const aut_config& c);
 
+// Whisper-style log-mel front end (16 kHz mono -> 128 bins, 100 frames/s).
+constexpr int LM_RATE = 16000;
+constexpr int LM_NFFT = 400;
+constexpr int LM_HOP = 160;
+constexpr int LM_MELS = 128;
+constexpr int LM_BIN_TILES = 13;  // 16-bin tiles covering the 201 DFT bins
+size_t logmel_table_floats();
+hipError_t launch_logmel_tables(float* tables, hipStream_t s);
+hipError_t launch_logmel(const float* audio, long s_max, const int* lens_dev, int B, int max_frames,
+                         const float* tables, float* feat, int T_max, unsigned* mx, hipStream_t s);
+
 // Audio rows into a decoder embedding sequence: dst[rows[j]] = audio[j].
 hipError_t launch_inject(const float* audio, const int* rows, long n, int dim, void* dst,
                          long dst_rows, aut_dtype dt, hipStream_t s);

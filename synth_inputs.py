@@ -116,6 +116,28 @@ def mel_features(lens, seed: int, pad_value: float = float("nan"),
     return x
 
 
+def audio_samples(n_samples, seed: int, s_max: int | None = None) -> np.ndarray:
+    """16 kHz mono stand-in for speech: Gaussian noise under a slowly varying,
+    log-normal envelope (pauses down to ~1e-4 of the loud parts) plus a few
+    steady tones, float32 [B, S_max]; samples past a request's length are 0."""
+    n = np.asarray(n_samples, dtype=np.int64)
+    B = len(n)
+    S = max(int(n.max()) if B else 1, 1) if s_max is None else int(s_max)
+    rng = np.random.default_rng([seed, 3])
+    x = np.zeros((B, S), dtype=np.float32)
+    for b in range(B):
+        L = int(n[b])
+        if not L:
+            continue
+        knots = rng.normal(0.0, 2.0, size=L // 1600 + 2)
+        env = np.exp(np.interp(np.arange(L) / 1600.0, np.arange(knots.size), knots))
+        t = np.arange(L) / 16000.0
+        tones = sum(rng.uniform(0.05, 0.3) * np.sin(2 * np.pi * rng.uniform(80, 7000) * t + rng.uniform(0, 6.3))
+                    for _ in range(3))
+        x[b, :L] = (0.1 * env * rng.normal(size=L) + tones).astype(np.float32)
+    return x
+
+
 def param_shapes(cfg: dict) -> list[tuple[str, tuple]]:
     """Parameter roles in generation order, PyTorch layouts ([out, in(, kH, kW)])."""
     C = cfg["downsample_hidden_size"]
