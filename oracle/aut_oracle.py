@@ -210,6 +210,104 @@ def window_attention(q, k, v, cu_seqlens, num_heads: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# 8-bit matrix products: MX-fp8 operands
+# ---------------------------------------------------------------------------
+# The pages run 8-bit variants of the encoder and judge them by the per-token
+# cosine similarity to the full-precision one (soniqo "Qwen3-ASR" transcribe
+# guide, es, section "Codificador CoreML (Neural Engine)": an INT8-palettised
+# encoder at cosine > 0.999; the 8-, 5- and 4-bit MLX rows of its performance
+# table).  Those formats are weight-only and Apple-specific.  The reading taken
+# here is the 8-bit format the gfx950 matrix cores multiply at twice the bf16
+# rate, OCP MX-fp8 (OCP "Microscaling Formats (MX) v1.0"): both operands of a
+# product in e4m3 (OCP "8-bit Floating Point" E4M3: sign, 4 exponent bits with
+# bias 7, 3 mantissa bits, subnormals, no infinities, S.1111.111 = NaN,
+# largest finite 448), every 32 consecutive values along the contraction axis
+# sharing one power-of-two scale stored as E8M0 (scale = 2^(code - 127)).  The
+# MX format leaves the choice of scale to the quantizer; here it is the
+# smallest power of two s with max|x| / s <= 448 over the block (no element
+# saturates), and each x / s goes to the nearest e4m3 value, ties to the even
+# code.  Everything outside the products stays as in the unquantized path.
+
+E4M3_MAX = 448.0
+MX_BLOCK = 32
+FP8_QKV, FP8_OUT, FP8_FC1, FP8_FC2, FP8_PROJ = 1, 2, 4, 8, 16
+FP8_ALL = 31
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each e4m3 code (uint8): exponent field 0 is subnormal,
+    (m / 8) 2^-6; otherwise (1 + m / 8) 2^(e - 7); S.1111.111 is NaN."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest e4m3 code of each |x| <= 448 (ties to the even code; -0.0 and
+    +0.0 both give code 0 after a zero round: the sign of a zero is kept)."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > E4M3_MAX) or np.any(np.isnan(x)):
+        raise ValueError("e4m3_encode: |x| > 448 or NaN")
+    vals = e4m3_decode(np.arange(127))                     # 0 .. 448, ascending
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, 126)   # vals[hi] >= a
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == vals[hi], hi, code)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def mx_block_exponent(amax) -> np.ndarray:
+    """Smallest integer e with amax <= 448 * 2^e, within the E8M0 range
+    [-127, 127]; an all-zero block takes -127."""
+    a = np.asarray(amax, dtype=np.float64)
+    safe = np.where(a > 0, a, E4M3_MAX)
+    e = np.ceil(np.log2(safe / E4M3_MAX))
+    e = np.where(safe > E4M3_MAX * np.exp2(e), e + 1, e)            # log2 rounding
+    e = np.where(safe <= E4M3_MAX * np.exp2(e - 1), e - 1, e)
+    e = np.where(a > 0, e, -127)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def mx_quantize(x):
+    """x [..., K] with K a multiple of 32 -> (e4m3 codes uint8 [..., K],
+    E8M0 scale codes uint8 [..., K / 32]), blocks along the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    if K % MX_BLOCK:
+        raise ValueError("mx_quantize: K must be a multiple of 32")
+    xb = x.reshape(x.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    e = mx_block_exponent(np.abs(xb).max(axis=-1))
+    codes = e4m3_encode(xb / np.exp2(e)[..., None])
+    return codes.reshape(x.shape), (e + 127).astype(np.uint8)
+
+
+def mx_dequantize(codes, scales) -> np.ndarray:
+    c = np.asarray(codes)
+    K = c.shape[-1]
+    v = e4m3_decode(c).reshape(c.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    s = np.exp2(np.asarray(scales, dtype=np.float64) - 127.0)
+    return (v * s[..., None]).reshape(c.shape)
+
+
+def mx_round(x) -> np.ndarray:
+    """x after an MX-fp8 round trip."""
+    return mx_dequantize(*mx_quantize(x))
+
+
+def linear_mx(x: np.ndarray, w: np.ndarray, b=None) -> np.ndarray:
+    """``linear`` with both operands MX-fp8 rounded along the contraction axis
+    (rows of x, rows of W in its [out, in] layout); exact products and sums."""
+    return linear(mx_round(x), mx_round(np.asarray(w, dtype=np.float64)), b)
+
+
+# ---------------------------------------------------------------------------
 # the encoder
 # ---------------------------------------------------------------------------
 
@@ -262,37 +360,43 @@ def frontend(features, feature_lens, P: dict, cfg: dict, chunk_ids=None):
     return np.zeros((0, d)), pl
 
 
-def encoder_layer(x: np.ndarray, cu_seqlens, P: dict, i: int, cfg: dict):
+def _lin(fp8: int, bit: int):
+    """The product of one GEMM class: MX-fp8 operands when its bit is set."""
+    return linear_mx if fp8 & bit else linear
+
+
+def encoder_layer(x: np.ndarray, cu_seqlens, P: dict, i: int, cfg: dict, fp8: int = 0):
     """One pre-LN layer: x += Attn(LN1 x); x += FFN(LN2 x) with
-    FFN(y) = fc2(GELU(fc1 y)).  qkv rows are [q; k; v]."""
+    FFN(y) = fc2(GELU(fc1 y)).  qkv rows are [q; k; v].  ``fp8``: FP8_* bits
+    of the products that take MX-fp8 operands."""
     p = f"layers.{i}."
     d = cfg["d_model"]
     h = layer_norm(x, P[p + "ln1_g"], P[p + "ln1_b"])
-    qkv = linear(h, P[p + "qkv_w"], P.get(p + "qkv_b"))
+    qkv = _lin(fp8, FP8_QKV)(h, P[p + "qkv_w"], P.get(p + "qkv_b"))
     q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
     o = window_attention(q, k, v, cu_seqlens, cfg["encoder_attention_heads"])
-    x = x + linear(o, P[p + "o_w"], P.get(p + "o_b"))
+    x = x + _lin(fp8, FP8_OUT)(o, P[p + "o_w"], P.get(p + "o_b"))
     h = layer_norm(x, P[p + "ln2_g"], P[p + "ln2_b"])
-    f = gelu(linear(h, P[p + "fc1_w"], P.get(p + "fc1_b")))
-    x = x + linear(f, P[p + "fc2_w"], P.get(p + "fc2_b"))
+    f = gelu(_lin(fp8, FP8_FC1)(h, P[p + "fc1_w"], P.get(p + "fc1_b")))
+    x = x + _lin(fp8, FP8_FC2)(f, P[p + "fc2_w"], P.get(p + "fc2_b"))
     return x
 
 
-def encode(hidden: np.ndarray, cu_seqlens, P: dict, cfg: dict) -> np.ndarray:
+def encode(hidden: np.ndarray, cu_seqlens, P: dict, cfg: dict, fp8: int = 0) -> np.ndarray:
     """m-star ``encode``: the layer stack and projector over a packed
     sequence, (total_tokens, d_model) -> (total_tokens, output_dim)."""
     x = np.asarray(hidden, dtype=np.float64)
     for i in range(cfg["encoder_layers"]):
-        x = encoder_layer(x, cu_seqlens, P, i, cfg)
+        x = encoder_layer(x, cu_seqlens, P, i, cfg, fp8)
     y = layer_norm(x, P["ln_post_g"], P["ln_post_b"])
-    y = gelu(linear(y, P["proj1_w"], P.get("proj1_b")))
-    return linear(y, P["proj2_w"], P.get("proj2_b"))
+    y = gelu(_lin(fp8, FP8_PROJ)(y, P["proj1_w"], P.get("proj1_b")))
+    return _lin(fp8, FP8_PROJ)(y, P["proj2_w"], P.get("proj2_b"))
 
 
-def forward(features, feature_lens, P: dict, cfg: dict):
+def forward(features, feature_lens, P: dict, cfg: dict, fp8: int = 0):
     """m-star ``forward``: (output [total_tokens, output_dim], layout)."""
     hidden, pl = frontend(features, feature_lens, P, cfg)
-    return encode(hidden, pl["cu_seqlens"], P, cfg), pl
+    return encode(hidden, pl["cu_seqlens"], P, cfg, fp8), pl
 
 
 def window_chunks(pl: dict, cfg: dict) -> list[list[int]]:

@@ -362,6 +362,60 @@ def check_log_mel():
     return max(e, abs(ao.frames_for_samples(16000) - 100) * 1.0)
 
 
+def torch_mx_round(x, block=32):
+    """MX-fp8 round trip built independently: the block exponent by a search
+    over every E8M0 value, the element rounding by torch's float8_e4m3fn."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    xb = x.reshape(-1, block)
+    out = np.empty_like(xb)
+    for i, blk in enumerate(xb):
+        amax = np.abs(blk).max()
+        e = -127
+        while e < 127 and amax > 448.0 * 2.0 ** e:
+            e += 1
+        t = torch.from_numpy((blk / 2.0 ** e).astype(np.float32)).to(torch.float8_e4m3fn)
+        out[i] = t.to(torch.float64).numpy() * 2.0 ** e
+    return out.reshape(x.shape)
+
+
+def check_e4m3():
+    r = np.random.default_rng(5)
+    x = (r.uniform(-1, 1, 20000) * np.exp2(r.integers(-12, 9, 20000))).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    vals = ao.e4m3_decode(np.arange(127)).astype(np.float32)
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)        # exact in fp32
+    x = np.concatenate([x, mids, -mids, vals])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return float(np.count_nonzero(ao.e4m3_encode(x.astype(np.float64)) != ref))
+
+
+def check_mx():
+    r = np.random.default_rng(6)
+    x = r.standard_normal((24, 128)) * np.exp2(r.integers(-20, 20, (24, 1)))
+    x[3, 32:64] = 0.0
+    x[5, :32] = 448.0 * 2.0 ** -3              # block maximum exactly on a scale boundary
+    # e4m3 rounding is scale-free except below the normal range: blocks whose
+    # first value dwarfs the rest put the others into the subnormal range
+    x[7:12] = r.standard_normal((5, 128)) * 2.0 ** -14
+    x[7:12, ::32] = 1.0
+    x = x.astype(np.float32).astype(np.float64)
+    try:
+        got = ao.mx_round(x)
+    except ValueError:                          # an element past the e4m3 range
+        return float("inf")
+    d = np.abs(got - torch_mx_round(x)).reshape(-1, 32)
+    return float((d / np.abs(x).reshape(-1, 32).max(1, keepdims=True).clip(1e-300)).max())
+
+
+def check_linear_mx():
+    r = np.random.default_rng(7)
+    x = r.standard_normal((16, 96)).astype(np.float32).astype(np.float64)
+    w = (r.standard_normal((40, 96)) * 0.02).astype(np.float32).astype(np.float64)
+    b = r.standard_normal(40)
+    ref = torch_mx_round(x) @ torch_mx_round(w).T + b
+    return float(np.abs(ao.linear_mx(x, w, b) - ref).max())
+
+
 MUTATIONS = {
     "conv kernel transposed": ("conv2d_k3s2p1", lambda orig: (lambda x, w, b: orig(x, np.swapaxes(w, 2, 3), b)), check_conv),
     "conv bias dropped": ("conv2d_k3s2p1", lambda orig: (lambda x, w, b: orig(x, w, np.zeros_like(b))), check_conv),
@@ -385,7 +439,20 @@ MUTATIONS = {
     "last frame kept": ("frames_for_samples", lambda orig: (lambda n: int(n) // 160 + 1), check_log_mel),
     "natural log": ("log_mel", lambda orig: _log_mel_ln, check_log_mel),
     "floor at max - 10": ("log_mel", lambda orig: _log_mel_floor10, check_log_mel),
+    "e4m3 truncated": ("e4m3_encode", lambda orig: _e4m3_trunc, check_e4m3),
+    "e4m3 ties away from zero": ("e4m3_encode", lambda orig: (lambda x: orig(np.clip(np.asarray(x, dtype=np.float64) * (1 + 2.0 ** -40), -448, 448))), check_e4m3),
+    "mx block of 16": ("MX_BLOCK", lambda orig: 16, check_mx),
+    "mx floor exponent rule": ("mx_block_exponent", lambda orig: (lambda a: np.where(np.asarray(a) > 0, np.floor(np.log2(np.where(np.asarray(a) > 0, a, 1.0))) - 8, -127).astype(np.int64)), check_mx),
+    "mx scale bias 128": ("mx_dequantize", lambda orig: (lambda c, sc: orig(c, np.asarray(sc, dtype=np.int64) - 1)), check_mx),
+    "mx weights left unquantized": ("linear_mx", lambda orig: (lambda x, w, b=None: ao.linear(ao.mx_round(x), w, b)), check_linear_mx),
 }
+
+
+def _e4m3_trunc(x):
+    x = np.asarray(x, dtype=np.float64)
+    vals = ao.e4m3_decode(np.arange(127))
+    code = np.searchsorted(vals, np.abs(x), side="right") - 1
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
 
 
 def _log_mel_ln(audio, n_mels=128):
@@ -423,7 +490,7 @@ def _pe_wrong_inc(n, c):
     return np.concatenate([np.sin(t), np.cos(t)], 1)
 
 
-def _post_ln_layer(x, cu, P, i, cfg):
+def _post_ln_layer(x, cu, P, i, cfg, fp8=0):
     p = f"layers.{i}."
     d = cfg["d_model"]
     qkv = ao.linear(x, P[p + "qkv_w"], P[p + "qkv_b"])
@@ -558,3 +625,89 @@ def test_log_mel_floor_and_scale():
     lg = torch.clamp(mel, min=1e-10).log10()
     lg = torch.maximum(lg, lg.max() - 8.0)
     np.testing.assert_allclose(ao.log_mel(x), ((lg + 4.0) / 4.0).numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# MX-fp8 products (OCP 8-bit floating point and Microscaling formats)
+# ---------------------------------------------------------------------------
+
+
+def test_e4m3_decode_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    got = ao.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    # closed forms of the format: largest finite, smallest subnormal and normal, one, NaNs
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6 and got[0x38] == 1.0
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and np.count_nonzero(np.isnan(got)) == 2
+    assert np.all(np.diff(got[:127]) > 0)
+
+
+def test_e4m3_encode_vs_torch():
+    assert check_e4m3() == 0
+
+
+def test_e4m3_ties_to_even():
+    x = np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 432.0, -1.0625, 0.0])
+    assert list(ao.e4m3_encode(x)) == [0x38, 0x3A, 0x00, 0x02, 0x7E, 0xB8, 0x00]
+    with pytest.raises(ValueError):
+        ao.e4m3_encode(np.array([449.0]))
+
+
+def test_mx_block_exponent_brute_force():
+    r = np.random.default_rng(8)
+    a = np.concatenate([r.uniform(0, 1, 400) * np.exp2(r.integers(-60, 60, 400)),
+                        448.0 * np.exp2(np.arange(-20, 20, dtype=np.float64)),
+                        np.nextafter(448.0 * np.exp2(np.arange(-20, 20, dtype=np.float64)), np.inf),
+                        [0.0, 1e-300, 1e300]])
+    got = ao.mx_block_exponent(a)
+    for ai, e in zip(a, got):
+        want = -127
+        while want < 127 and ai > 448.0 * 2.0 ** want:
+            want += 1
+        assert e == want, (ai, e, want)
+
+
+def test_mx_quantize_matches_independent_build():
+    assert check_mx() == 0
+
+
+def test_mx_quantize_bounds_and_representable_identity():
+    r = np.random.default_rng(9)
+    x = r.standard_normal((64, 256))
+    codes, sc = ao.mx_quantize(x)
+    v = ao.e4m3_decode(codes).reshape(64, 8, 32)
+    amax = np.abs(v).max(-1)
+    assert np.all((amax >= 224) & (amax <= 448))             # the smallest scale that fits
+    q = ao.mx_dequantize(codes, sc)
+    rel = np.abs(q - x) / np.abs(x)
+    assert rel[np.abs(x) > np.repeat(np.abs(x).reshape(64, 8, 32).max(-1), 32, 1) / 2**6].max() <= 2.0 ** -4
+    # MX-representable input: the round trip is the identity
+    assert np.array_equal(ao.mx_round(q), q)
+    assert np.array_equal(ao.linear_mx(q, q[:16]), q @ q[:16].T)
+
+
+def test_linear_mx_vs_independent_build():
+    assert check_linear_mx() < 1e-12
+
+
+def test_fp8_encoder_masks():
+    cfg = small_cfg(encoder_layers=1)
+    lens = np.array([420], dtype=np.int32)
+    feats = si.mel_features(lens, seed=3)
+    P = si.params(cfg, seed=4)
+    base, _ = ao.forward(feats, lens, P, cfg)
+    same, _ = ao.forward(feats, lens, P, cfg, fp8=0)
+    assert np.array_equal(base, same)
+    cos_all = None
+    for bit in (ao.FP8_QKV, ao.FP8_OUT, ao.FP8_FC1, ao.FP8_FC2, ao.FP8_PROJ, ao.FP8_ALL):
+        out, _ = ao.forward(feats, lens, P, cfg, fp8=bit)
+        assert not np.array_equal(out, base)
+        cos = (out * base).sum(1) / np.linalg.norm(out, axis=1) / np.linalg.norm(base, axis=1)
+        assert cos.min() > 0.99, (bit, cos.min())
+        if bit == ao.FP8_ALL:
+            cos_all = cos.min()
+    assert cos_all < 0.99999
