@@ -207,6 +207,48 @@ def stream_latency(aut, torch, cfg, packed, dtype, feats, steps, append=100):
                     "re-encodes at most one 8 s window plus the new chunks"}
 
 
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 (MX-fp8) matrix peak
+
+
+def fp8_rate(aut, torch, cfg_d, P, fd, lens, steps, mask):
+    """The same workload under AUT_FP8 with the products of `mask` on MX-fp8
+    operands: ms per step and the fp8 products' rate against the fp8 peak."""
+    cfg = aut.config(dict(cfg_d, fp8_gemms=mask))
+    dev = {k: torch.from_numpy(v).cuda() for k, v in P.items()}
+    packed = aut.weights_pack(cfg, dev, "fp8")
+    del dev
+    pl = aut.plan(cfg, lens)
+    T = pl.total_tokens
+    ws = aut.workspace(cfg, pl, "fp8")
+    out = torch.empty((T, cfg.output_dim), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        aut.encode(cfg, fd, lens, packed, "fp8", out=out, ws=ws)
+    torch.cuda.synchronize()
+    aut.profile_collect()
+    aut.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        aut.encode(cfg, fd, lens, packed, "fp8", out=out, ws=ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    aut.profile_enable(False)
+    st = aut.profile_collect()
+    ms = (t1 - t0) * 1e3 / steps
+    g8 = st["gemm_fp8"]
+    res = {"fp8_gemms": mask, "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3),
+           "audio_s_per_s": float(np.sum(lens)) / 100.0 / (ms / 1e3)}
+    if g8["launches"]:
+        sec = g8["total_ms"] / 1e3
+        res.update(gemm_fp8_tflops=g8["flops"] / sec / 1e12, gemm_fp8_peak=PEAK_FP8_TFLOPS,
+                   gemm_fp8_frac=g8["flops"] / sec / 1e12 / PEAK_FP8_TFLOPS,
+                   gemm_fp8_ms_per_step=g8["total_ms"] / steps,
+                   gemm_fp8_avg_us=1e3 * g8["total_ms"] / g8["launches"])
+    if st["gemm"]["launches"]:
+        res["gemm_bf16_ms_per_step"] = st["gemm"]["total_ms"] / steps
+    del ws, packed, out
+    return res
+
+
 def cpu_baseline(name, cfg_d, lens, feats, P, n_windows):
     """The float64 oracle on a bounded sample of the same workload's windows."""
     import oracle
@@ -243,6 +285,8 @@ def main():
     ap.add_argument("--workload", default="wide", choices=list(si.WORKLOADS))
     ap.add_argument("--cpu-windows", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8-steps", type=int, default=5,
+                    help="steps of the AUT_FP8 legs (0: skip them)")
     ap.add_argument("--stream-steps", type=int, default=30,
                     help="1 s appends timed for the incremental-encode latency (0: skip)")
     ap.add_argument("--no-kernel-events", action="store_true",
@@ -398,6 +442,13 @@ def main():
     if args.stream_steps > 0:
         res["stream"] = stream_latency(aut, torch, cfg, packed, dtype, feats, args.stream_steps)
         log(f"stream: {res['stream']['step_ms_p50']:.3f} ms per 1 s append (p50)")
+    if args.fp8_steps > 0 and dtype == "bf16":
+        # all encoder and projector products on MX-fp8, and the q/k/v
+        # projection alone (the mask that keeps the pages' cosine > 0.999)
+        res["fp8"] = [fp8_rate(aut, torch, cfg_d, P, fd, lens, args.fp8_steps, m) for m in (31, 1)]
+        for r in res["fp8"]:
+            log(f"fp8 mask {r['fp8_gemms']}: {r['ms_per_step']:.3f} ms/step, "
+                f"fp8 products {r.get('gemm_fp8_tflops', 0):.0f} TFLOP/s")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on sampled windows)")
         res["cpu_baseline"] = cpu_baseline(name, cfg_d, lens, feats, P, args.cpu_windows)

@@ -52,8 +52,28 @@ typedef enum {
 /* Arithmetic type of the matrix products.  AUT_FP32: every operand and every
  * activation is fp32.  AUT_BF16: GEMM/conv/attention operands are bf16
  * (round to nearest even), accumulation, LayerNorm statistics, softmax and
- * the residual stream stay fp32. */
-typedef enum { AUT_FP32 = 0, AUT_BF16 = 1 } aut_dtype;
+ * the residual stream stay fp32.  AUT_FP8: as AUT_BF16, except that the
+ * encoder-layer and projector products named by aut_config.fp8_gemms take
+ * MX-fp8 operands (OCP Microscaling formats: e4m3 elements, one power-of-two
+ * E8M0 scale per 32 consecutive values along the contraction axis, the
+ * smallest scale with no element above 448, elements rounded to nearest
+ * even), quantized by the kernel that produces each operand; accumulation
+ * stays fp32.  The 8-bit variants on the pages (soniqo "Qwen3-ASR" transcribe
+ * guide: the INT8 CoreML encoder, the 8/5/4-bit MLX rows of the performance
+ * table) are weight-only formats of Apple hardware; this is the 8-bit format
+ * the gfx950 matrix cores multiply at twice the bf16 rate.  Requires d_model
+ * and encoder_ffn_dim multiples of 128. */
+typedef enum { AUT_FP32 = 0, AUT_BF16 = 1, AUT_FP8 = 2 } aut_dtype;
+
+/* aut_config.fp8_gemms bits: the products that run on MX-fp8 under AUT_FP8. */
+enum {
+  AUT_FP8_QKV = 1,   /* fused q/k/v projection (operand: LayerNorm 1 output) */
+  AUT_FP8_OUT = 2,   /* attention output projection (operand: attention output) */
+  AUT_FP8_FC1 = 4,   /* FFN fc1 (operand: LayerNorm 2 output) */
+  AUT_FP8_FC2 = 8,   /* FFN fc2 (operand: GELU(fc1) output) */
+  AUT_FP8_PROJ = 16, /* projector proj1 and proj2 */
+  AUT_FP8_ALL = 31
+};
 
 /* Model hyper-parameters.  Field names and defaults follow AuTEncoderConfig
  * on the m-star API page; ln_eps and conv_out_bias are additions (LayerNorm
@@ -76,6 +96,7 @@ typedef struct {
   int32_t max_source_positions;   /* 1500: sinusoid table length */
   int32_t conv_out_bias;          /* 0: conv_out has no bias; 1: it has one */
   float ln_eps;                   /* 1e-5 */
+  int32_t fp8_gemms;              /* AUT_FP8_* bits, read under AUT_FP8 only; default AUT_FP8_ALL */
 } aut_config;
 
 /* One chunk of the plan: which request it belongs to, its first mel frame,
@@ -303,6 +324,39 @@ aut_status aut_audio_rows(const int32_t* ids, int64_t n_ids, int32_t pad_id, int
 aut_status aut_inject_audio(const float* audio, const int32_t* rows, int64_t n_audio, int32_t dim,
                             void* dst, int64_t dst_rows, aut_dtype dst_dtype, void* stream);
 
+/* ------------------------------------------------------------------------
+ * MX-fp8 operands (the AUT_FP8 products) as primitives: the conversion the
+ * packing and the operand-producing kernels apply, and one product.
+ * Format: OCP Microscaling MX-fp8, e4m3 codes (OCP 8-bit floating point) and
+ * one E8M0 scale code per 32 consecutive values of a row, scale 2^(code-127),
+ * the smallest power of two with no element above 448; elements rounded to
+ * nearest even.  Scale layout of an operand with R rows and K columns (K a
+ * multiple of 128): rows padded to a multiple of 16; the scale of row r, block
+ * kb (columns 32 kb .. 32 kb + 31) is byte
+ *   ((r / 16) * (K / 128) + kb / 4) * 64 + (kb % 4) * 16 + r % 16,
+ * i.e. per 16 rows and 128 columns the 64 bytes one scaled matrix instruction
+ * takes, in lane order.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of the scale array of an operand with `rows` rows and K columns:
+ * ceil(rows / 16) * 16 * K / 32.  K must be a positive multiple of 128. */
+aut_status aut_mx_scale_bytes(int64_t rows, int32_t K, size_t* bytes);
+
+/* x: device fp32 [rows, K], row-major, 16-byte aligned -> codes: device uint8
+ * [rows, K] (16-byte aligned), scales: device, aut_mx_scale_bytes(rows, K)
+ * bytes (the padding rows get scale code 0).  |x| must be finite.
+ * Asynchronous on `stream`. */
+aut_status aut_mx_quantize(const float* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                           void* stream);
+
+/* out: device fp32 [M, N] = A B^T with A = (a_codes [M, K], a_scales) and
+ * B = (b_codes [N, K], b_scales) as produced by aut_mx_quantize; products
+ * exact, sums in fp32.  K a multiple of 128, N a multiple of 4, codes and out
+ * 16-byte aligned.  Asynchronous on `stream`. */
+aut_status aut_mx_matmul(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M,
+                         const uint8_t* b_codes, const uint8_t* b_scales, int32_t N, int32_t K,
+                         float* out, void* stream);
+
 /* Kernel classes for the optional per-launch timing below. */
 typedef enum {
   AUT_K_CONV1 = 0,     /* conv1 (+GELU), fp32 vector ALU */
@@ -312,7 +366,8 @@ typedef enum {
   AUT_K_GEMM = 4,      /* qkv / out_proj / fc1 / fc2 / proj1 / proj2 */
   AUT_K_ATTENTION = 5, /* window attention */
   AUT_K_LOGMEL = 6,    /* log-mel front end (DFT + filterbank + log, floor pass) */
-  AUT_K_COUNT = 7
+  AUT_K_GEMM_FP8 = 7,  /* the AUT_K_GEMM products on MX-fp8 operands */
+  AUT_K_COUNT = 8
 } aut_kernel_class;
 
 typedef struct {

@@ -263,6 +263,19 @@ def e4m3_encode(x) -> np.ndarray:
     return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
 
 
+def e4m3_round(x) -> np.ndarray:
+    """The value ``e4m3_encode`` picks, computed directly: |x| <= 448 rounded
+    to a multiple of its binade's spacing 2^(max(E, -6) - 3), E = floor(log2
+    |x|) (3 mantissa bits; below 2^-6 the fixed subnormal spacing 2^-9), ties
+    to even by np.rint, sign kept."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > E4M3_MAX):
+        raise ValueError("e4m3_round: |x| > 448")
+    _, E = np.frexp(x)                       # |x| = m 2^E, m in [0.5, 1)
+    q = np.maximum(E - 1, -6) - 3
+    return np.ldexp(np.rint(np.ldexp(x, -q)), q)
+
+
 def mx_block_exponent(amax) -> np.ndarray:
     """Smallest integer e with amax <= 448 * 2^e, within the E8M0 range
     [-127, 127]; an all-zero block takes -127."""
@@ -297,14 +310,36 @@ def mx_dequantize(codes, scales) -> np.ndarray:
 
 
 def mx_round(x) -> np.ndarray:
-    """x after an MX-fp8 round trip."""
-    return mx_dequantize(*mx_quantize(x))
+    """x after an MX-fp8 round trip, mx_dequantize(*mx_quantize(x)), computed
+    on values: each block's scale exponent, then e4m3_round of x / 2^e."""
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    if K % MX_BLOCK:
+        raise ValueError("mx_round: K must be a multiple of 32")
+    xb = x.reshape(x.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    e = mx_block_exponent(np.abs(xb).max(axis=-1))[..., None]
+    return np.ldexp(e4m3_round(np.ldexp(xb, -e)), e).reshape(x.shape)
+
+
+_MX_WEIGHTS: dict = {}
+
+
+def _mx_weight(w) -> np.ndarray:
+    """mx_round of a parameter array, remembered per array object (a
+    parameter is rounded once however many windows or calls use it)."""
+    hit = _MX_WEIGHTS.get(id(w))
+    if hit is None or hit[0] is not w:
+        if len(_MX_WEIGHTS) > 512:
+            _MX_WEIGHTS.clear()
+        hit = (w, mx_round(np.asarray(w, dtype=np.float64)))
+        _MX_WEIGHTS[id(w)] = hit
+    return hit[1]
 
 
 def linear_mx(x: np.ndarray, w: np.ndarray, b=None) -> np.ndarray:
     """``linear`` with both operands MX-fp8 rounded along the contraction axis
     (rows of x, rows of W in its [out, in] layout); exact products and sums."""
-    return linear(mx_round(x), mx_round(np.asarray(w, dtype=np.float64)), b)
+    return linear(mx_round(x), _mx_weight(w), b)
 
 
 # ---------------------------------------------------------------------------
@@ -416,7 +451,7 @@ def window_chunks(pl: dict, cfg: dict) -> list[list[int]]:
     return out
 
 
-def forward_windows(features, feature_lens, P: dict, cfg: dict, windows):
+def forward_windows(features, feature_lens, P: dict, cfg: dict, windows, fp8: int = 0):
     """Exact output rows of selected windows only.
 
     Windows are independent end to end (block-diagonal attention, per-row
@@ -430,7 +465,7 @@ def forward_windows(features, feature_lens, P: dict, cfg: dict, windows):
         ids = wch[w]
         hidden, _ = frontend(features, feature_lens, P, cfg, chunk_ids=ids)
         n = hidden.shape[0]
-        res[w] = (pl["cu_seqlens"][w], encode(hidden, [0, n], P, cfg))
+        res[w] = (pl["cu_seqlens"][w], encode(hidden, [0, n], P, cfg, fp8))
     return res
 
 

@@ -16,8 +16,12 @@ LIB_PATH = os.path.join(_PKG, "libaut.so")
 AUT_OK = 0
 STATUS = {0: "AUT_OK", 1: "AUT_ERR_INVALID_ARG", 2: "AUT_ERR_UNSUPPORTED",
           3: "AUT_ERR_MISSING_WEIGHT", 4: "AUT_ERR_WORKSPACE_TOO_SMALL", 5: "AUT_ERR_HIP"}
-DTYPES = {"fp32": 0, "bf16": 1}
-KERNEL_CLASSES = ["conv1", "conv_gemm", "conv_out", "layernorm", "gemm", "attention", "logmel"]
+DTYPES = {"fp32": 0, "bf16": 1, "fp8": 2}
+KERNEL_CLASSES = ["conv1", "conv_gemm", "conv_out", "layernorm", "gemm", "attention", "logmel",
+                  "gemm_fp8"]
+# aut_config.fp8_gemms bits (the products on MX-fp8 operands under "fp8")
+FP8_QKV, FP8_OUT, FP8_FC1, FP8_FC2, FP8_PROJ = 1, 2, 4, 8, 16
+FP8_ALL = 31
 
 CONFIG_FIELDS = ["d_model", "encoder_layers", "encoder_attention_heads", "encoder_ffn_dim",
                  "num_mel_bins", "n_window", "n_window_infer", "conv_chunksize",
@@ -25,7 +29,8 @@ CONFIG_FIELDS = ["d_model", "encoder_layers", "encoder_attention_heads", "encode
 
 
 class AutConfig(ctypes.Structure):
-    _fields_ = [(f, c_int32) for f in CONFIG_FIELDS] + [("ln_eps", c_float)]
+    _fields_ = ([(f, c_int32) for f in CONFIG_FIELDS] + [("ln_eps", c_float)]
+                + [("fp8_gemms", c_int32)])
 
 
 class AutChunk(ctypes.Structure):
@@ -83,6 +88,10 @@ SIGNATURES = {
     "aut_logmel_workspace_bytes": (c_int, [c_int32, POINTER(c_size_t)]),
     "aut_logmel": (c_int, [c_void_p, c_int32, POINTER(c_int32), c_int32, c_void_p, c_void_p, c_int32,
                            c_void_p, c_size_t, c_void_p]),
+    "aut_mx_scale_bytes": (c_int, [c_int64, c_int32, POINTER(c_size_t)]),
+    "aut_mx_quantize": (c_int, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
+    "aut_mx_matmul": (c_int, [c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_int32,
+                              c_void_p, c_void_p]),
     "aut_profile_enable": (c_int, [c_int]),
     "aut_profile_collect": (c_int, [POINTER(AutKernelStats)]),
     "aut_last_error": (c_char_p, []),
@@ -137,6 +146,8 @@ def config(cfg: dict | None = None, **over) -> AutConfig:
             setattr(c, f, int(src[f]))
     if "ln_eps" in src:
         c.ln_eps = float(src["ln_eps"])
+    if "fp8_gemms" in src:
+        c.fp8_gemms = int(src["fp8_gemms"])
     return c
 
 
@@ -384,3 +395,45 @@ def profile_collect() -> dict:
     _check(lib().aut_profile_collect(st))
     return {n: dict(launches=s.launches, total_ms=s.total_ms, flops=s.flops, bytes=s.bytes)
             for n, s in zip(KERNEL_CLASSES, st)}
+
+
+def mx_scale_bytes(rows: int, K: int) -> int:
+    n = c_size_t()
+    _check(lib().aut_mx_scale_bytes(int(rows), int(K), byref(n)))
+    return n.value
+
+
+def mx_quantize(x, stream=None):
+    """aut_mx_quantize: fp32 [R, K] on the device -> (e4m3 codes uint8 [R, K],
+    scale codes uint8 in the kernels' layout, mx_scale_bytes(R, K) bytes)."""
+    if str(x.dtype) != "torch.float32" or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D float32 tensor")
+    import torch
+    R, K = x.shape
+    codes = torch.empty((R, K), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(max(1, mx_scale_bytes(R, K)), dtype=torch.uint8, device=x.device)
+    _check(lib().aut_mx_quantize(_ptr(x), R, K, _ptr(codes), _ptr(scales), _stream_ptr(stream)))
+    return codes, scales
+
+
+def mx_scales_rowmajor(scales, rows: int, K: int):
+    """The kernels' scale layout as [rows, K / 32] (host-side reindexing)."""
+    import numpy as np
+    s = np.asarray(scales)
+    r = np.arange(rows)[:, None]
+    kb = np.arange(K // 32)[None, :]
+    idx = ((r // 16) * (K // 128) + kb // 4) * 64 + (kb % 4) * 16 + r % 16
+    return s[idx]
+
+
+def mx_matmul(a_codes, a_scales, b_codes, b_scales, out=None, stream=None):
+    """aut_mx_matmul: out fp32 [M, N] = A B^T on MX-fp8 operands (codes
+    [M, K] and [N, K] with their scales in the kernels' layout)."""
+    import torch
+    M, K = a_codes.shape
+    N = b_codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    _check(lib().aut_mx_matmul(_ptr(a_codes), _ptr(a_scales), M, _ptr(b_codes), _ptr(b_scales), N,
+                               K, _ptr(out), _stream_ptr(stream)))
+    return out

@@ -35,7 +35,13 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int half_up(int n) { return (n + 1) / 2; }  // Conv2d(k3, s2, p1) output length
 
-size_t esize(aut_dtype dt) { return dt == AUT_BF16 ? 2 : 4; }
+// activation element size: fp32, or bf16 (also under AUT_FP8, whose MX-fp8
+// operands take one byte plus 1/32 of a scale byte per element and fit in the
+// same buffers)
+size_t esize(aut_dtype dt) { return dt == AUT_FP32 ? 4 : 2; }
+
+// the arithmetic of everything that is not an MX-fp8 product
+aut_dtype base_dtype(aut_dtype dt) { return dt == AUT_FP8 ? AUT_BF16 : dt; }
 
 }  // namespace
 
@@ -152,6 +158,7 @@ extern "C" aut_status aut_config_default(aut_config* cfg) {
   cfg->max_source_positions = 1500;
   cfg->conv_out_bias = 0;
   cfg->ln_eps = 1e-5f;
+  cfg->fp8_gemms = AUT_FP8_ALL;
   return AUT_OK;
 }
 
@@ -165,6 +172,8 @@ extern "C" aut_status aut_config_check(const aut_config* c) {
   if (!(c->ln_eps > 0.f)) return fail(AUT_ERR_INVALID_ARG, "ln_eps must be positive");
   if (c->conv_out_bias != 0 && c->conv_out_bias != 1)
     return fail(AUT_ERR_INVALID_ARG, "conv_out_bias must be 0 or 1");
+  if (c->fp8_gemms < 0 || c->fp8_gemms > AUT_FP8_ALL)
+    return fail(AUT_ERR_INVALID_ARG, "fp8_gemms must be a combination of AUT_FP8_* bits");
   Geometry g = aut::geometry(*c);
   if (c->num_mel_bins != 128) return fail(AUT_ERR_UNSUPPORTED, "num_mel_bins must be 128");
   if (g.cf > 256) return fail(AUT_ERR_UNSUPPORTED, "2 * n_window must be <= 256");
@@ -278,18 +287,25 @@ extern "C" void aut_plan_destroy(aut_plan_t* plan) { delete plan; }
 
 namespace {
 
+// A GEMM weight [rows, cols] is bf16/fp32, or under AUT_FP8 with its class
+// bit set, MX-fp8 codes at *_w and scales at *_s.
 struct LayerOff {
   size_t ln1_g, ln1_b, qkv_w, qkv_b, o_w, o_b, ln2_g, ln2_b, fc1_w, fc1_b, fc2_w, fc2_b;
+  size_t qkv_s, o_s, fc1_s, fc2_s;
 };
 
 struct PackLayout {
   size_t conv1_w, conv1_b, conv2_w, conv2_b, conv3_w, conv3_b, conv_out_w, conv_out_b, pe;
   std::vector<LayerOff> layers;
   size_t ln_post_g, ln_post_b, proj1_w, proj1_b, proj2_w, proj2_b;
+  size_t proj1_s, proj2_s;
   size_t total;
 };
 
-PackLayout pack_layout(const Geometry& g, aut_dtype dt) {
+// the AUT_FP8_* bits in force for a dtype
+int fp8_mask(const aut_config& c, aut_dtype dt) { return dt == AUT_FP8 ? c.fp8_gemms : 0; }
+
+PackLayout pack_layout(const Geometry& g, aut_dtype dt, int f8) {
   PackLayout L;
   size_t off = 0;
   const size_t es = esize(dt);
@@ -297,6 +313,16 @@ PackLayout pack_layout(const Geometry& g, aut_dtype dt) {
     size_t o = off;
     off = align256(off + bytes);
     return o;
+  };
+  // a GEMM weight: codes and scales when its class runs on MX-fp8
+  auto wmat = [&](size_t& w, size_t& sc, size_t rows, size_t cols, int bit) {
+    if (f8 & bit) {
+      w = take(rows * cols);
+      sc = take(aut::mx_scale_bytes((long)rows, (int)cols));
+    } else {
+      w = take(rows * cols * es);
+      sc = 0;
+    }
   };
   const size_t C = g.C, d = g.d, F = g.F, O = g.out;
   L.conv1_w = take(C * 9 * 4);
@@ -313,37 +339,46 @@ PackLayout pack_layout(const Geometry& g, aut_dtype dt) {
     LayerOff& l = L.layers[i];
     l.ln1_g = take(d * 4);
     l.ln1_b = take(d * 4);
-    l.qkv_w = take(3 * d * d * es);
+    wmat(l.qkv_w, l.qkv_s, 3 * d, d, AUT_FP8_QKV);
     l.qkv_b = take(3 * d * 4);
-    l.o_w = take(d * d * es);
+    wmat(l.o_w, l.o_s, d, d, AUT_FP8_OUT);
     l.o_b = take(d * 4);
     l.ln2_g = take(d * 4);
     l.ln2_b = take(d * 4);
-    l.fc1_w = take(F * d * es);
+    wmat(l.fc1_w, l.fc1_s, F, d, AUT_FP8_FC1);
     l.fc1_b = take(F * 4);
-    l.fc2_w = take(d * F * es);
+    wmat(l.fc2_w, l.fc2_s, d, F, AUT_FP8_FC2);
     l.fc2_b = take(d * 4);
   }
   L.ln_post_g = take(d * 4);
   L.ln_post_b = take(d * 4);
-  L.proj1_w = take(d * d * es);
+  wmat(L.proj1_w, L.proj1_s, d, d, AUT_FP8_PROJ);
   L.proj1_b = take(d * 4);
-  L.proj2_w = take(O * d * es);
+  wmat(L.proj2_w, L.proj2_s, O, d, AUT_FP8_PROJ);
   L.proj2_b = take(O * 4);
   L.total = off;
   return L;
 }
 
-bool valid_dtype(aut_dtype dt) { return dt == AUT_FP32 || dt == AUT_BF16; }
+bool valid_dtype(aut_dtype dt) { return dt == AUT_FP32 || dt == AUT_BF16 || dt == AUT_FP8; }
+
+// what the MX-fp8 products need of the sizes: k steps of 128 for every
+// product whose operand is d_model or encoder_ffn_dim wide
+aut_status check_dtype(const aut_config& c, aut_dtype dt) {
+  if (!valid_dtype(dt)) return fail(AUT_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (dt == AUT_FP8 && (c.d_model % 128 || c.encoder_ffn_dim % 128))
+    return fail(AUT_ERR_UNSUPPORTED, "AUT_FP8 needs d_model and encoder_ffn_dim multiples of 128");
+  return AUT_OK;
+}
 
 }  // namespace
 
 extern "C" aut_status aut_weights_bytes(const aut_config* cfg, aut_dtype dtype, size_t* bytes) {
   aut_status st = aut_config_check(cfg);
   if (st != AUT_OK) return st;
-  if (!valid_dtype(dtype)) return fail(AUT_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if ((st = check_dtype(*cfg, dtype)) != AUT_OK) return st;
   if (!bytes) return fail(AUT_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = pack_layout(aut::geometry(*cfg), dtype).total;
+  *bytes = pack_layout(aut::geometry(*cfg), dtype, fp8_mask(*cfg, dtype)).total;
   return AUT_OK;
 }
 
@@ -351,11 +386,12 @@ extern "C" aut_status aut_weights_pack(const aut_config* cfg, const aut_weight_p
                                        aut_dtype dt, void* dst, size_t dst_bytes, void* stream) {
   aut_status st = aut_config_check(cfg);
   if (st != AUT_OK) return st;
-  if (!valid_dtype(dt)) return fail(AUT_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if ((st = check_dtype(*cfg, dt)) != AUT_OK) return st;
   if (!w) return fail(AUT_ERR_INVALID_ARG, "weights is NULL");
   if (!dst) return fail(AUT_ERR_INVALID_ARG, "dst is NULL");
   const Geometry g = aut::geometry(*cfg);
-  const PackLayout L = pack_layout(g, dt);
+  const int f8 = fp8_mask(*cfg, dt);
+  const PackLayout L = pack_layout(g, dt, f8);
   if (dst_bytes < L.total)
     return fail(AUT_ERR_WORKSPACE_TOO_SMALL, "packed buffer has %zu bytes, needs %zu", dst_bytes,
                 L.total);
@@ -395,20 +431,28 @@ extern "C" aut_status aut_weights_pack(const aut_config* cfg, const aut_weight_p
 
   hipStream_t s = (hipStream_t)stream;
   char* base = (char*)dst;
+  const aut_dtype bdt = base_dtype(dt);
   auto vec = [&](const float* src, size_t off, int n) {
     return aut::launch_pack(src, base + off, AUT_FP32, aut::PACK_CAST, 1, n, 0, 0, s);
   };
   auto mat = [&](const float* src, size_t off, int rows, int cols) {
-    return aut::launch_pack(src, base + off, dt, aut::PACK_CAST, rows, cols, 0, 0, s);
+    return aut::launch_pack(src, base + off, bdt, aut::PACK_CAST, rows, cols, 0, 0, s);
+  };
+  // a GEMM weight, MX-fp8 when its class bit is set
+  auto gmat = [&](const float* src, size_t off, size_t off_s, int rows, int cols, int bit) {
+    if (f8 & bit)
+      return aut::launch_mx_quantize(src, cols, rows, cols, (uint8_t*)(base + off),
+                                     (uint8_t*)(base + off_s), s);
+    return mat(src, off, rows, cols);
   };
   const int C = g.C, d = g.d, F = g.F;
   HIPCHK(aut::launch_pack(w->conv1_w, base + L.conv1_w, AUT_FP32, aut::PACK_CAST, C, 9, 0, 0, s));
   HIPCHK(vec(w->conv1_b, L.conv1_b, C));
-  HIPCHK(aut::launch_pack(w->conv2_w, base + L.conv2_w, dt, aut::PACK_CONV, C, 9 * C, C, 0, s));
+  HIPCHK(aut::launch_pack(w->conv2_w, base + L.conv2_w, bdt, aut::PACK_CONV, C, 9 * C, C, 0, s));
   HIPCHK(vec(w->conv2_b, L.conv2_b, C));
-  HIPCHK(aut::launch_pack(w->conv3_w, base + L.conv3_w, dt, aut::PACK_CONV, C, 9 * C, C, 0, s));
+  HIPCHK(aut::launch_pack(w->conv3_w, base + L.conv3_w, bdt, aut::PACK_CONV, C, 9 * C, C, 0, s));
   HIPCHK(vec(w->conv3_b, L.conv3_b, C));
-  HIPCHK(aut::launch_pack(w->conv_out_w, base + L.conv_out_w, dt, aut::PACK_CONV_OUT, d,
+  HIPCHK(aut::launch_pack(w->conv_out_w, base + L.conv_out_w, bdt, aut::PACK_CONV_OUT, d,
                           g.h3 * C, C, g.h3, s));
   if (cfg->conv_out_bias) HIPCHK(vec(w->conv_out_b, L.conv_out_b, d));
   HIPCHK(aut::launch_pe_table((float*)(base + L.pe), g.w3, d, s));
@@ -416,22 +460,22 @@ extern "C" aut_status aut_weights_pack(const aut_config* cfg, const aut_weight_p
     const LayerOff& l = L.layers[i];
     HIPCHK(vec(w->ln1_g[i], l.ln1_g, d));
     HIPCHK(vec(w->ln1_b[i], l.ln1_b, d));
-    HIPCHK(mat(w->qkv_w[i], l.qkv_w, 3 * d, d));
+    HIPCHK(gmat(w->qkv_w[i], l.qkv_w, l.qkv_s, 3 * d, d, AUT_FP8_QKV));
     HIPCHK(vec(w->qkv_b[i], l.qkv_b, 3 * d));
-    HIPCHK(mat(w->o_w[i], l.o_w, d, d));
+    HIPCHK(gmat(w->o_w[i], l.o_w, l.o_s, d, d, AUT_FP8_OUT));
     HIPCHK(vec(w->o_b[i], l.o_b, d));
     HIPCHK(vec(w->ln2_g[i], l.ln2_g, d));
     HIPCHK(vec(w->ln2_b[i], l.ln2_b, d));
-    HIPCHK(mat(w->fc1_w[i], l.fc1_w, F, d));
+    HIPCHK(gmat(w->fc1_w[i], l.fc1_w, l.fc1_s, F, d, AUT_FP8_FC1));
     HIPCHK(vec(w->fc1_b[i], l.fc1_b, F));
-    HIPCHK(mat(w->fc2_w[i], l.fc2_w, d, F));
+    HIPCHK(gmat(w->fc2_w[i], l.fc2_w, l.fc2_s, d, F, AUT_FP8_FC2));
     HIPCHK(vec(w->fc2_b[i], l.fc2_b, d));
   }
   HIPCHK(vec(w->ln_post_g, L.ln_post_g, d));
   HIPCHK(vec(w->ln_post_b, L.ln_post_b, d));
-  HIPCHK(mat(w->proj1_w, L.proj1_w, d, d));
+  HIPCHK(gmat(w->proj1_w, L.proj1_w, L.proj1_s, d, d, AUT_FP8_PROJ));
   HIPCHK(vec(w->proj1_b, L.proj1_b, d));
-  HIPCHK(mat(w->proj2_w, L.proj2_w, g.out, d));
+  HIPCHK(gmat(w->proj2_w, L.proj2_w, L.proj2_s, g.out, d, AUT_FP8_PROJ));
   HIPCHK(vec(w->proj2_b, L.proj2_b, g.out));
   return AUT_OK;
 }
@@ -446,6 +490,7 @@ struct WsLayout {
   size_t chunks, rowmap, cu, worder;
   size_t a1, a2, a3;
   size_t x, xn, qkv, o, h;
+  size_t xn_s, o_s, h_s;  // AUT_FP8: MX scales of xn, o and h
   size_t total;
   int nb;  // chunks per conv-stem batch
 };
@@ -481,6 +526,12 @@ WsLayout ws_layout(const aut_plan_t& p, aut_dtype dt) {
   W.qkv = take(T * 3 * g.d * es);
   W.o = take(T * g.d * es);
   W.h = take(T * std::max(g.F, g.d) * es);
+  W.xn_s = W.o_s = W.h_s = 0;
+  if (dt == AUT_FP8 && T > 0) {
+    W.xn_s = take(aut::mx_scale_bytes((long)T, g.d));
+    W.o_s = take(aut::mx_scale_bytes((long)T, g.d));
+    W.h_s = take(aut::mx_scale_bytes((long)T, std::max(g.F, g.d)));
+  }
   W.total = off;
   return W;
 }
@@ -490,7 +541,7 @@ aut_status check_common(const aut_config* cfg, const aut_plan_t* plan, aut_dtype
   aut_status st = aut_config_check(cfg);
   if (st != AUT_OK) return st;
   if (!plan) return fail(AUT_ERR_INVALID_ARG, "plan is NULL");
-  if (!valid_dtype(dt)) return fail(AUT_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if ((st = check_dtype(*cfg, dt)) != AUT_OK) return st;
   if (memcmp(cfg, &plan->cfg, sizeof(aut_config)) != 0)
     return fail(AUT_ERR_INVALID_ARG, "plan was made for a different configuration");
   *W = ws_layout(*plan, dt);
@@ -511,7 +562,7 @@ extern "C" aut_status aut_workspace_bytes(const aut_config* cfg, const aut_plan_
   aut_status st = aut_config_check(cfg);
   if (st != AUT_OK) return st;
   if (!plan) return fail(AUT_ERR_INVALID_ARG, "plan is NULL");
-  if (!valid_dtype(dtype)) return fail(AUT_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if ((st = check_dtype(*cfg, dtype)) != AUT_OK) return st;
   if (!bytes) return fail(AUT_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = ws_layout(*plan, dtype).total;
   return AUT_OK;
@@ -546,12 +597,13 @@ namespace {
 struct Ctx {
   const aut_plan_t* p;
   const Geometry* g;
-  aut_dtype dt;
+  aut_dtype dt;  // arithmetic outside the MX-fp8 products (bf16 under AUT_FP8)
   const PackLayout* P;
   const WsLayout* W;
   const char* pk;  // packed parameters
   char* ws;        // workspace
   hipStream_t s;
+  int f8;          // AUT_FP8_* bits of the products on MX-fp8 operands
 };
 
 template <typename X>
@@ -563,6 +615,14 @@ aut_status gemm(const Ctx& c, aut_kernel_class cls, const aut::GemmArgs& a, int 
   hipError_t e = aut::launch_gemm(a, amode, epi, c.dt, c.s);
   if (e != hipSuccess) return fail(AUT_ERR_HIP, "gemm launch failed: %s", hipGetErrorString(e));
   aut::prof_end(c.s, cls, 2.0 * a.M * (double)a.N * a.K, bytes);
+  return AUT_OK;
+}
+
+aut_status gemm_f8(const Ctx& c, const aut::GemmArgs& a, int epi, double bytes) {
+  aut::prof_begin(c.s);
+  hipError_t e = aut::launch_gemm_f8(a, epi, c.s);
+  if (e != hipSuccess) return fail(AUT_ERR_HIP, "fp8 gemm launch failed: %s", hipGetErrorString(e));
+  aut::prof_end(c.s, AUT_K_GEMM_FP8, 2.0 * a.M * (double)a.N * a.K, bytes);
   return AUT_OK;
 }
 
@@ -650,17 +710,24 @@ aut_status run_frontend(const Ctx& c, const float* feat, int T_max, float* hidde
   return AUT_OK;
 }
 
-aut_status layernorm(const Ctx& c, const float* x, size_t g_off, size_t b_off, void* y) {
+// LayerNorm into the next product's operand: MX-fp8 (codes in y, scales in
+// ysc) when ysc is given
+aut_status layernorm(const Ctx& c, const float* x, size_t g_off, size_t b_off, void* y,
+                     uint8_t* ysc = nullptr) {
   const int T = (int)c.p->total, d = c.g->d;
   aut::prof_begin(c.s);
   hipError_t e = aut::launch_layernorm(x, pk_at<float>(c, g_off), pk_at<float>(c, b_off), y, T, d,
-                                       c.p->cfg.ln_eps, c.dt, c.s);
+                                       c.p->cfg.ln_eps, ysc ? AUT_FP8 : c.dt, c.s, ysc);
   if (e != hipSuccess) return fail(AUT_ERR_HIP, "layernorm launch failed: %s", hipGetErrorString(e));
-  aut::prof_end(c.s, AUT_K_LAYERNORM, 8.0 * T * d, (double)T * d * (4 + esize(c.dt)));
+  aut::prof_end(c.s, AUT_K_LAYERNORM, 8.0 * T * d,
+                (double)T * d * (4 + (ysc ? 1.0 + 1.0 / 32 : (double)esize(c.dt))));
   return AUT_OK;
 }
 
-// encoder stack + projector: ws.x (fp32 residual, in place) -> out [T, out]
+// encoder stack + projector: ws.x (fp32 residual, in place) -> out [T, out].
+// A product on MX-fp8 operands (its AUT_FP8_* bit set) gets its activation
+// operand from the kernel that produces it (LayerNorm, attention or the GELU
+// epilogue of fc1 / proj1) as codes plus scales, and its weight as packed.
 aut_status run_encode(const Ctx& c, float* out) {
   const aut_plan_t& p = *c.p;
   const Geometry& g = *c.g;
@@ -670,44 +737,68 @@ aut_status run_encode(const Ctx& c, float* out) {
   if (T == 0) return AUT_OK;
   const int d = g.d, F = g.F;
   const double es = (double)esize(c.dt);
+  const double e8 = 1.0 + 1.0 / 32;  // bytes per MX-fp8 element with its scale
   float* x = (float*)(c.ws + W.x);
   void* xn = c.ws + W.xn;
   void* qkv = c.ws + W.qkv;
   void* o = c.ws + W.o;
   void* h = c.ws + W.h;
+  uint8_t* xn_s = (uint8_t*)(c.ws + W.xn_s);
+  uint8_t* o_s = (uint8_t*)(c.ws + W.o_s);
+  uint8_t* h_s = (uint8_t*)(c.ws + W.h_s);
+  const bool f_qkv = c.f8 & AUT_FP8_QKV, f_out = c.f8 & AUT_FP8_OUT;
+  const bool f_fc1 = c.f8 & AUT_FP8_FC1, f_fc2 = c.f8 & AUT_FP8_FC2;
+  const bool f_proj = c.f8 & AUT_FP8_PROJ;
+  // one product: MX-fp8 operands (scales of A and B) or the base dtype
+  // (out_s: the output's scales when the epilogue writes MX-fp8)
+  auto prod = [&](bool f8, aut::GemmArgs a, const uint8_t* a_s, size_t b_s, int epi,
+                  uint8_t* out_s, double bytes_base, double bytes_f8) {
+    a.out_scale = out_s;
+    if (!f8) return gemm(c, AUT_K_GEMM, a, aut::A_PLAIN, epi, bytes_base);
+    a.a_scale = a_s;
+    a.b_scale = (const uint8_t*)(c.pk + b_s);
+    return gemm_f8(c, a, epi, bytes_f8);
+  };
   aut_status st;
   for (int i = 0; i < g.layers; ++i) {
     const LayerOff& l = P.layers[i];
-    if ((st = layernorm(c, x, l.ln1_g, l.ln1_b, xn)) != AUT_OK) return st;
-    st = gemm(c, AUT_K_GEMM,
-              plain_args(xn, c.pk + l.qkv_w, T, 3 * d, d, pk_at<float>(c, l.qkv_b), qkv, 3 * d),
-              aut::A_PLAIN, aut::EPI_STORE, ((double)T * d + 3.0 * d * d + 3.0 * T * d) * es);
+    if ((st = layernorm(c, x, l.ln1_g, l.ln1_b, xn, f_qkv ? xn_s : nullptr)) != AUT_OK) return st;
+    st = prod(f_qkv, plain_args(xn, c.pk + l.qkv_w, T, 3 * d, d, pk_at<float>(c, l.qkv_b), qkv, 3 * d),
+              xn_s, l.qkv_s, aut::EPI_STORE, nullptr,
+              ((double)T * d + 3.0 * d * d + 3.0 * T * d) * es,
+              ((double)T * d + 3.0 * d * d) * e8 + 3.0 * T * d * es);
     if (st != AUT_OK) return st;
     aut::prof_begin(c.s);
     hipError_t e = aut::launch_attention(qkv, o, (const int*)(c.ws + W.cu),
                                          (const int*)(c.ws + W.worder), (int)p.cu.size() - 1, g.H,
-                                         d, c.dt, c.s);
+                                         d, f_out ? AUT_FP8 : c.dt, c.s, f_out ? o_s : nullptr);
     if (e != hipSuccess) return fail(AUT_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
-    aut::prof_end(c.s, AUT_K_ATTENTION, 4.0 * d * p.sum_len2, 4.0 * T * d * es);
-    st = gemm(c, AUT_K_GEMM, plain_args(o, c.pk + l.o_w, T, d, d, pk_at<float>(c, l.o_b), x, d),
-              aut::A_PLAIN, aut::EPI_RESID, ((double)T * d + (double)d * d) * es + 8.0 * T * d);
+    aut::prof_end(c.s, AUT_K_ATTENTION, 4.0 * d * p.sum_len2, 3.0 * T * d * es + T * d * (f_out ? e8 : es));
+    st = prod(f_out, plain_args(o, c.pk + l.o_w, T, d, d, pk_at<float>(c, l.o_b), x, d), o_s, l.o_s,
+              aut::EPI_RESID, nullptr, ((double)T * d + (double)d * d) * es + 8.0 * T * d,
+              ((double)T * d + (double)d * d) * e8 + 8.0 * T * d);
     if (st != AUT_OK) return st;
-    if ((st = layernorm(c, x, l.ln2_g, l.ln2_b, xn)) != AUT_OK) return st;
-    st = gemm(c, AUT_K_GEMM, plain_args(xn, c.pk + l.fc1_w, T, F, d, pk_at<float>(c, l.fc1_b), h, F),
-              aut::A_PLAIN, aut::EPI_STORE_GELU, ((double)T * d + (double)F * d + (double)T * F) * es);
+    if ((st = layernorm(c, x, l.ln2_g, l.ln2_b, xn, f_fc1 ? xn_s : nullptr)) != AUT_OK) return st;
+    // fc1 writes GELU(.) as the operand of fc2: MX-fp8 when fc2 runs on it
+    st = prod(f_fc1, plain_args(xn, c.pk + l.fc1_w, T, F, d, pk_at<float>(c, l.fc1_b), h, F), xn_s,
+              l.fc1_s, f_fc2 ? aut::EPI_GELU_MX : aut::EPI_STORE_GELU, f_fc2 ? h_s : nullptr,
+              ((double)T * d + (double)F * d) * es + (double)T * F * (f_fc2 ? e8 : es),
+              ((double)T * d + (double)F * d) * e8 + (double)T * F * (f_fc2 ? e8 : es));
     if (st != AUT_OK) return st;
-    st = gemm(c, AUT_K_GEMM, plain_args(h, c.pk + l.fc2_w, T, d, F, pk_at<float>(c, l.fc2_b), x, d),
-              aut::A_PLAIN, aut::EPI_RESID, ((double)T * F + (double)d * F) * es + 8.0 * T * d);
+    st = prod(f_fc2, plain_args(h, c.pk + l.fc2_w, T, d, F, pk_at<float>(c, l.fc2_b), x, d), h_s,
+              l.fc2_s, aut::EPI_RESID, nullptr, ((double)T * F + (double)d * F) * es + 8.0 * T * d,
+              ((double)T * F + (double)d * F) * e8 + 8.0 * T * d);
     if (st != AUT_OK) return st;
   }
-  if ((st = layernorm(c, x, P.ln_post_g, P.ln_post_b, xn)) != AUT_OK) return st;
-  st = gemm(c, AUT_K_GEMM, plain_args(xn, c.pk + P.proj1_w, T, d, d, pk_at<float>(c, P.proj1_b), h, d),
-            aut::A_PLAIN, aut::EPI_STORE_GELU, (2.0 * T * d + (double)d * d) * es);
+  if ((st = layernorm(c, x, P.ln_post_g, P.ln_post_b, xn, f_proj ? xn_s : nullptr)) != AUT_OK) return st;
+  st = prod(f_proj, plain_args(xn, c.pk + P.proj1_w, T, d, d, pk_at<float>(c, P.proj1_b), h, d), xn_s,
+            P.proj1_s, f_proj ? aut::EPI_GELU_MX : aut::EPI_STORE_GELU, f_proj ? h_s : nullptr,
+            (2.0 * T * d + (double)d * d) * es, (2.0 * T * d + (double)d * d) * e8);
   if (st != AUT_OK) return st;
-  st = gemm(c, AUT_K_GEMM,
-            plain_args(h, c.pk + P.proj2_w, T, g.out, d, pk_at<float>(c, P.proj2_b), out, g.out),
-            aut::A_PLAIN, aut::EPI_STORE_F32,
-            ((double)T * d + (double)g.out * d) * es + 4.0 * T * g.out);
+  st = prod(f_proj, plain_args(h, c.pk + P.proj2_w, T, g.out, d, pk_at<float>(c, P.proj2_b), out, g.out),
+            h_s, P.proj2_s, aut::EPI_STORE_F32, nullptr,
+            ((double)T * d + (double)g.out * d) * es + 4.0 * T * g.out,
+            ((double)T * d + (double)g.out * d) * e8 + 4.0 * T * g.out);
   return st;
 }
 
@@ -732,8 +823,9 @@ extern "C" aut_status aut_encode_planned(const aut_config* cfg, const aut_plan_t
   if ((st = check_features(features, T_max, *plan)) != AUT_OK) return st;
   if (plan->total > 0 && !out) return fail(AUT_ERR_INVALID_ARG, "out is NULL");
   if (plan->total == 0) return AUT_OK;
-  const PackLayout P = pack_layout(plan->geo, dt);
-  Ctx c{plan, &plan->geo, dt, &P, &W, (const char*)packed, (char*)ws, (hipStream_t)stream};
+  const PackLayout P = pack_layout(plan->geo, dt, fp8_mask(plan->cfg, dt));
+  Ctx c{plan, &plan->geo, base_dtype(dt), &P, &W, (const char*)packed, (char*)ws,
+        (hipStream_t)stream, fp8_mask(plan->cfg, dt)};
   if ((st = run_frontend(c, features, T_max, (float*)((char*)ws + W.x))) != AUT_OK) return st;
   return run_encode(c, out);
 }
@@ -748,8 +840,9 @@ extern "C" aut_status aut_frontend(const aut_config* cfg, const aut_plan_t* plan
   if ((st = check_features(features, T_max, *plan)) != AUT_OK) return st;
   if (plan->total > 0 && !hidden) return fail(AUT_ERR_INVALID_ARG, "hidden is NULL");
   if (plan->total == 0) return AUT_OK;
-  const PackLayout P = pack_layout(plan->geo, dt);
-  Ctx c{plan, &plan->geo, dt, &P, &W, (const char*)packed, (char*)ws, (hipStream_t)stream};
+  const PackLayout P = pack_layout(plan->geo, dt, fp8_mask(plan->cfg, dt));
+  Ctx c{plan, &plan->geo, base_dtype(dt), &P, &W, (const char*)packed, (char*)ws,
+        (hipStream_t)stream, fp8_mask(plan->cfg, dt)};
   return run_frontend(c, features, T_max, hidden);
 }
 
@@ -761,8 +854,9 @@ extern "C" aut_status aut_encode_packed(const aut_config* cfg, const aut_plan_t*
   if (st != AUT_OK) return st;
   if (plan->total == 0) return AUT_OK;
   if (!hidden || !out) return fail(AUT_ERR_INVALID_ARG, "hidden or out is NULL");
-  const PackLayout P = pack_layout(plan->geo, dt);
-  Ctx c{plan, &plan->geo, dt, &P, &W, (const char*)packed, (char*)ws, (hipStream_t)stream};
+  const PackLayout P = pack_layout(plan->geo, dt, fp8_mask(plan->cfg, dt));
+  Ctx c{plan, &plan->geo, base_dtype(dt), &P, &W, (const char*)packed, (char*)ws,
+        (hipStream_t)stream, fp8_mask(plan->cfg, dt)};
   HIPCHK(hipMemcpyAsync((char*)ws + W.x, hidden, (size_t)plan->total * plan->geo.d * 4,
                         hipMemcpyDeviceToDevice, c.s));
   return run_encode(c, out);
@@ -971,6 +1065,58 @@ extern "C" aut_status aut_inject_audio(const float* audio, const int32_t* rows, 
   hipError_t e = aut::launch_inject(audio, rows, (long)n_audio, dim, dst, (long)dst_rows, dst_dtype,
                                     (hipStream_t)stream);
   if (e != hipSuccess) return fail(AUT_ERR_HIP, "inject launch failed: %s", hipGetErrorString(e));
+  return AUT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// MX-fp8 primitives
+// ---------------------------------------------------------------------------
+
+extern "C" aut_status aut_mx_scale_bytes(int64_t rows, int32_t K, size_t* bytes) {
+  if (!bytes) return fail(AUT_ERR_INVALID_ARG, "bytes is NULL");
+  if (rows < 0 || K <= 0 || K % 128)
+    return fail(AUT_ERR_INVALID_ARG, "need rows >= 0 and K a positive multiple of 128");
+  *bytes = aut::mx_scale_bytes((long)rows, K);
+  return AUT_OK;
+}
+
+extern "C" aut_status aut_mx_quantize(const float* x, int64_t rows, int32_t K, uint8_t* codes,
+                                      uint8_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 128)
+    return fail(AUT_ERR_INVALID_ARG, "need rows >= 0 and K a positive multiple of 128");
+  if (rows == 0) return AUT_OK;
+  if (!x || !codes || !scales) return fail(AUT_ERR_INVALID_ARG, "NULL pointer");
+  if (((size_t)x & 15) || ((size_t)codes & 15))
+    return fail(AUT_ERR_INVALID_ARG, "x and codes must be 16-byte aligned");
+  if (rows * (int64_t)K >= ((int64_t)1 << 40)) return fail(AUT_ERR_INVALID_ARG, "too large");
+  hipError_t e = aut::launch_mx_quantize(x, K, (long)rows, K, codes, scales, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AUT_ERR_HIP, "mx quantize launch failed: %s", hipGetErrorString(e));
+  return AUT_OK;
+}
+
+extern "C" aut_status aut_mx_matmul(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M,
+                                    const uint8_t* b_codes, const uint8_t* b_scales, int32_t N,
+                                    int32_t K, float* out, void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 128)
+    return fail(AUT_ERR_INVALID_ARG, "need M, N >= 0 and K a positive multiple of 128");
+  if (M == 0 || N == 0) return AUT_OK;
+  if (N % 4) return fail(AUT_ERR_UNSUPPORTED, "N must be a multiple of 4");
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !out)
+    return fail(AUT_ERR_INVALID_ARG, "NULL pointer");
+  if (((size_t)a_codes & 15) || ((size_t)b_codes & 15) || ((size_t)out & 15))
+    return fail(AUT_ERR_INVALID_ARG, "codes and out must be 16-byte aligned");
+  // 32-bit buffer offsets inside the kernel
+  if (M * (int64_t)K >= ((int64_t)1 << 31) || (int64_t)N * K >= ((int64_t)1 << 31) ||
+      M > ((int64_t)1 << 30))
+    return fail(AUT_ERR_UNSUPPORTED, "operands of 2 GiB or more");
+  aut::GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.A = a_codes; a.lda = K; a.B = b_codes; a.ldb = K;
+  a.M = (int)M; a.N = N; a.K = K;
+  a.out = out; a.ldo = N;
+  a.a_scale = a_scales; a.b_scale = b_scales;
+  hipError_t e = aut::launch_gemm_f8(a, aut::EPI_STORE_F32, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AUT_ERR_HIP, "mx matmul launch failed: %s", hipGetErrorString(e));
   return AUT_OK;
 }
 

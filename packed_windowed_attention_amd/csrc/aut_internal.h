@@ -60,7 +60,10 @@ hipError_t launch_conv1(const float* feat, int T_max, const int* chunks, int chu
 // Generic MFMA GEMM: C[M, N] = A[M, K] * B[N, K]^T with an A-gather mode and
 // an epilogue.
 enum AMode { A_PLAIN = 0, A_CONV = 1, A_ROWMAP = 2 };
-enum Epi { EPI_STORE = 0, EPI_STORE_GELU = 1, EPI_RESID = 2, EPI_PE = 3, EPI_STORE_F32 = 4 };
+// EPI_GELU_MX: GELU, then MX-fp8 codes into `out` (ldo in bytes) and their
+// scales into `out_scale` (mx_scale_index layout over M rows and N columns).
+enum Epi { EPI_STORE = 0, EPI_STORE_GELU = 1, EPI_RESID = 2, EPI_PE = 3, EPI_STORE_F32 = 4,
+           EPI_GELU_MX = 5 };
 
 struct GemmArgs {
   const void* A; long lda;
@@ -78,6 +81,11 @@ struct GemmArgs {
   const float* bias;   // [N] or null
   void* out; long ldo;
   const float* pe;     // EPI_PE: [tpc, N] position rows, indexed rowmap[m] % tpc
+  // MX-fp8 products (launch_gemm_f8): scales of A (over M rows) and B (over N
+  // rows) in the mx_scale_index layout; EPI_GELU_MX: the output's scales
+  const uint8_t* a_scale;
+  const uint8_t* b_scale;
+  uint8_t* out_scale;
 };
 // bf16 runs the 256-row kernel (k_gemm256.hip), fp32 the 128 x 128 one
 // (k_gemm128.hip).
@@ -85,12 +93,26 @@ hipError_t launch_gemm(const GemmArgs& a, int amode, int epi, aut_dtype dt, hipS
 hipError_t launch_gemm128(const GemmArgs& a, int amode, int epi, aut_dtype dt, hipStream_t s);
 hipError_t launch_gemm256(const GemmArgs& a, int amode, int epi, hipStream_t s);
 
-// LayerNorm rows of fp32 x [T, d] into the GEMM operand type.
-hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, int T, int d,
-                            float eps, aut_dtype dt, hipStream_t s);
+// MX-fp8 products: A [M, K] and B [N, K] as e4m3 codes (lda, ldb in bytes)
+// with scales; K a multiple of 128.  Epilogues EPI_STORE, EPI_STORE_GELU,
+// EPI_RESID, EPI_STORE_F32, EPI_GELU_MX.
+hipError_t launch_gemm_f8(const GemmArgs& a, int epi, hipStream_t s);
 
-// Window attention: qkv [T, 3d] (q | k | v) -> o [T, d].
+// fp32 rows [R, K] (row stride ldx) -> MX-fp8 codes [R, K] and scales
+// (mx_scale_bytes(R, K) bytes, rows padded to 16 with scale code 0).
+size_t mx_scale_bytes(long rows, int K);
+hipError_t launch_mx_quantize(const float* x, long ldx, long R, int K, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s);
+
+// LayerNorm rows of fp32 x [T, d] into the GEMM operand type; AUT_FP8: MX-fp8
+// codes into y and their scales into y_scales.
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, int T, int d,
+                            float eps, aut_dtype dt, hipStream_t s, uint8_t* y_scales = nullptr);
+
+// Window attention: qkv [T, 3d] (q | k | v) -> o [T, d].  AUT_FP8: bf16 qkv,
+// o as MX-fp8 codes with scales in o_scales.
 hipError_t launch_attention(const void* qkv, void* o, const int* cu, const int* worder,
-                            int n_windows, int H, int d, aut_dtype dt, hipStream_t s);
+                            int n_windows, int H, int d, aut_dtype dt, hipStream_t s,
+                            uint8_t* o_scales = nullptr);
 
 }  // namespace aut

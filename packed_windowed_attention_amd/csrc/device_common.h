@@ -102,3 +102,47 @@ __device__ __forceinline__ u32x4_t zero_unit() { return u32x4_t{0u, 0u, 0u, 0u};
 __device__ __forceinline__ u32x4_t ldg_unit(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
+
+// ------------------------------- MX-fp8 ------------------------------------
+// OCP Microscaling MX-fp8: e4m3 elements (OCP 8-bit floating point E4M3,
+// largest finite 448) in blocks of 32 consecutive values along a product's
+// contraction axis, each block with one power-of-two scale stored as E8M0
+// (scale = 2^(code - 127)).  The scale of a block is the smallest power of two
+// s with max|x| / s <= 448, so no element saturates.
+constexpr int MX_BLOCK = 32;
+
+// Byte of the scale of row r, block kb (k = 32 kb .. 32 kb + 31) of an operand
+// with K columns (K a multiple of 128): per 16-row group and 128-wide k step,
+// 64 bytes in the lane order of one scaled matrix instruction (lane
+// 16 (kb % 4) + r % 16).  Rows are padded to a multiple of 16.
+__device__ __forceinline__ size_t mx_scale_index(int r, int kb, int K) {
+  return ((size_t)(r >> 4) * (size_t)(K >> 7) + (size_t)(kb >> 2)) * 64 + (size_t)((kb & 3) * 16 + (r & 15));
+}
+
+// Exponent e of a block's scale 2^e: the smallest e with amax <= 448 * 2^e,
+// within [-127, 127] (an all-zero block gives -127).  Exact, from the bits:
+// amax = (1 + f) 2^E needs e = E - 8 when 1 + f <= 1.75, else E - 7.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const unsigned u = __builtin_bit_cast(unsigned, amax);
+  const int E = (int)(u >> 23) - 127;
+  const int e = E - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : e;  // zero and tiny blocks
+}
+
+// Four fp32 -> four e4m3 codes (round to nearest even; |x| <= 448), first
+// value in the lowest byte.
+__device__ __forceinline__ unsigned int pack_fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (unsigned int)w;
+}
+
+// x * 2^-e, exact
+__device__ __forceinline__ float mx_scale_down(float x, int e) { return __builtin_amdgcn_ldexpf(x, -e); }
+
+// The 32 fp8 bytes of a scaled matrix instruction's operand: two 16-byte units.
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+__device__ __forceinline__ i32x8_t units_to_i32x8(u32x4_t lo, u32x4_t hi) {
+  return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}

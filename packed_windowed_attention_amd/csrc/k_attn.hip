@@ -74,12 +74,38 @@ __device__ __forceinline__ void store_quad(float* p, float a, float b, float c, 
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 
-template <typename T>
+// MX-fp8 output of a query row's 64 head columns: a lane holds columns
+// 16 dt + 4 g + r (dt = 0..3, r = 0..3) of its query, so each 32-column block
+// (dt = 0, 1 or dt = 2, 3) is spread over the four lanes of the query's row
+// group; its maximum takes two shuffles across them.
+__device__ __forceinline__ void store_row_mx(uint8_t* orow, uint8_t* osc, int row, int col0, int d,
+                                             int g, const float (&v)[4][4], bool live) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    float amax = 0.f;
+#pragma unroll
+    for (int dt = 2 * blk; dt < 2 * blk + 2; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(v[dt][r]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    if (!live) continue;
+    const int e = mx_exponent(amax);
+#pragma unroll
+    for (int dt = 2 * blk; dt < 2 * blk + 2; ++dt)
+      *reinterpret_cast<unsigned int*>(orow + dt * 16 + 4 * g) =
+          pack_fp8x4(mx_scale_down(v[dt][0], e), mx_scale_down(v[dt][1], e),
+                     mx_scale_down(v[dt][2], e), mx_scale_down(v[dt][3], e));
+    if (g == blk) osc[mx_scale_index(row, (col0 >> 5) + blk, d)] = (uint8_t)(e + 127);
+  }
+}
+
+template <typename T, bool MX>
 __global__ __launch_bounds__(ATT_THREADS) void attn_kernel(const T* __restrict__ qkv,
-                                                          T* __restrict__ o,
+                                                          void* __restrict__ o_,
                                                           const int* __restrict__ cu,
                                                           const int* __restrict__ worder, int H,
-                                                          int d) {
+                                                          int d, uint8_t* __restrict__ osc) {
   constexpr int E = UnitElems<T>::value;  // elements per 16-byte unit
   constexpr int UR = 64 / E;              // units per head row
   constexpr int VS = VtStride<T>::value;
@@ -231,9 +257,17 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_kernel(const T* __restrict__
         for (int dt = 0; dt < 4; ++dt) mma16_k32(oacc[dt], vf[u][dt], pf);
       }
     }
-    if (i < L) {
-      const float inv = __builtin_amdgcn_rcpf(sum);
-      T* orow = o + (size_t)(s0 + i) * d + (size_t)h * 64;
+    const float inv = __builtin_amdgcn_rcpf(sum);
+    if constexpr (MX) {
+      float v[4][4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[dt][r] = oacc[dt][r] * inv;
+      store_row_mx((uint8_t*)o_ + (size_t)(s0 + i) * d + (size_t)h * 64, osc, s0 + i, h * 64, d, g,
+                   v, i < L);
+    } else if (i < L) {
+      T* orow = (T*)o_ + (size_t)(s0 + i) * d + (size_t)h * 64;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
         store_quad(orow + dt * 16 + 4 * g, oacc[dt][0] * inv, oacc[dt][1] * inv,
@@ -245,15 +279,21 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_kernel(const T* __restrict__
 }  // namespace
 
 hipError_t launch_attention(const void* qkv, void* o, const int* cu, const int* worder,
-                            int n_windows, int H, int d, aut_dtype dt, hipStream_t s) {
+                            int n_windows, int H, int d, aut_dtype dt, hipStream_t s,
+                            uint8_t* o_scales) {
   if (n_windows <= 0) return hipSuccess;
   dim3 grid(n_windows * H);
-  if (dt == AUT_BF16)
-    hipLaunchKernelGGL(attn_kernel<bf16_t>, grid, dim3(ATT_THREADS), 0, s, (const bf16_t*)qkv,
-                       (bf16_t*)o, cu, worder, H, d);
-  else
-    hipLaunchKernelGGL(attn_kernel<float>, grid, dim3(ATT_THREADS), 0, s, (const float*)qkv,
-                       (float*)o, cu, worder, H, d);
+  if (dt == AUT_FP8) {
+    if (d % 128 || !o_scales) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_kernel<bf16_t, true>), grid, dim3(ATT_THREADS), 0, s,
+                       (const bf16_t*)qkv, o, cu, worder, H, d, o_scales);
+  } else if (dt == AUT_BF16) {
+    hipLaunchKernelGGL((attn_kernel<bf16_t, false>), grid, dim3(ATT_THREADS), 0, s,
+                       (const bf16_t*)qkv, o, cu, worder, H, d, (uint8_t*)nullptr);
+  } else {
+    hipLaunchKernelGGL((attn_kernel<float, false>), grid, dim3(ATT_THREADS), 0, s,
+                       (const float*)qkv, o, cu, worder, H, d, (uint8_t*)nullptr);
+  }
   return hipGetLastError();
 }
 

@@ -94,7 +94,8 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& p, int m0, int n
                                                 u32x4_t* lds0, u32x4_t* lds1, u32x4_t* lds2,
                                                 u32x4_t* lds3) {
   constexpr int NTW = WN / 16;
-  constexpr bool F32 = EPI == EPI_RESID || EPI == EPI_PE || EPI == EPI_STORE_F32;
+  constexpr bool MX = EPI == EPI_GELU_MX;
+  constexpr bool F32 = EPI == EPI_RESID || EPI == EPI_PE || EPI == EPI_STORE_F32 || MX;
   constexpr int ES = F32 ? 4 : 2;          // output element size
   constexpr int PR = F32 ? 64 : 128;       // rows per pass
   constexpr int RB = PR / 4;               // rows per LDS buffer
@@ -139,7 +140,7 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& p, int m0, int n
         f32x4_t av = acc[j][i];
         asm volatile("" : "+v"(av));  // copy out of the accumulators one tile at a time
         float v[4] = {av[0] + bq[j].x, av[1] + bq[j].y, av[2] + bq[j].z, av[3] + bq[j].w};
-        if (EPI == EPI_STORE_GELU) {
+        if (EPI == EPI_STORE_GELU || MX) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = gelu_f(v[r]);
         }
@@ -153,6 +154,42 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& p, int m0, int n
       }
     }
     lds_barrier();
+    if constexpr (MX) {
+      // a thread per 32-value block of a staged row: its maximum, the scale
+      // exponent, 32 codes in two 16-byte stores and the scale byte
+      constexpr int BPR = BN / MX_BLOCK;
+#pragma unroll
+      for (int q = tid; q < PR * BPR; q += NT) {
+        const int r = q / BPR;
+        const int cb = q - r * BPR;
+        const int m = m0 + (r / HALF) * 128 + pass * HALF + r % HALF;
+        const int n = n0 + cb * MX_BLOCK;
+        const int b = r / RB;
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
+            (const char*)(b == 0 ? lds0 : b == 1 ? lds1 : b == 2 ? lds2 : lds3) + (r - b * RB) * PITCH +
+            cb * MX_BLOCK * 4);
+        f32x4_t f[8];
+        float amax = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          f[k] = __builtin_bit_cast(f32x4_t, src[k]);
+          amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f[k][0]), fabsf(f[k][1])), fmaxf(fabsf(f[k][2]), fabsf(f[k][3]))));
+        }
+        if (m < M && n < N) {
+          const int e = mx_exponent(amax);
+          unsigned int w[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            w[k] = pack_fp8x4(mx_scale_down(f[k][0], e), mx_scale_down(f[k][1], e),
+                              mx_scale_down(f[k][2], e), mx_scale_down(f[k][3], e));
+          u32x4_t* dst = reinterpret_cast<u32x4_t*>((uint8_t*)p.out + (size_t)m * p.ldo + n);
+          dst[0] = u32x4_t{w[0], w[1], w[2], w[3]};
+          dst[1] = u32x4_t{w[4], w[5], w[6], w[7]};
+          p.out_scale[mx_scale_index(m, n / MX_BLOCK, N)] = (uint8_t)(e + 127);
+        }
+      }
+      continue;
+    }
     // Copy-out in batches: every load of a batch (staged rows, residual or
     // position rows) is issued before any of its stores, so a batch waits for
     // the earlier stores once rather than once per chunk.
@@ -592,6 +629,144 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   staged_epilogue<BN, WN, NT8, EPI>(p, m0, n0, wm, wn, tid, acc, As0, As1, Bs0, Bs1);
 }
 
+// MX-fp8 variant of the eight-wave kernel (OCP Microscaling MX-fp8 operands:
+// e4m3 codes, one E8M0 scale per 32 values along k).  A k step is 128 codes
+// per row, the same 128 bytes per tile row as a bf16 step, so the LDS ring,
+// the swizzle and the direct loads are unchanged; one scaled matrix
+// instruction (v_mfma_scale_f32_16x16x128_f8f6f4, twice the bf16 rate)
+// consumes a whole step per 16 x 16 tile.  Its operand layout: lane l gives
+// row l % 16 and the bytes of k in [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g
+// + 16), g = l / 16 (row units g and g + 4), and the scale byte of row l % 16,
+// block g of the step.  The scales of a step are 64 consecutive bytes per
+// 16-row group (mx_scale_index), one byte load per lane per fragment, issued
+// with the step's tile loads.
+template <int BN, int EPI>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
+  constexpr int NT8 = 512;
+  constexpr int WN = BN / 4;                 // columns per wave
+  constexpr int NTW = WN / 16;               // 16-column tiles per wave
+  constexpr int A_UNITS = BM * KU;
+  constexpr int B_UNITS = BN * KU;
+  constexpr int A_LOADS = A_UNITS / NT8;
+  constexpr int B_LOADS = B_UNITS / NT8;
+  constexpr int BK8 = 128;                   // codes per row per k step
+  static_assert(B_UNITS % NT8 == 0, "whole B loads per thread");
+  __shared__ u32x4_t As0[A_UNITS], As1[A_UNITS];
+  __shared__ u32x4_t Bs0[B_UNITS], Bs1[B_UNITS];
+
+  const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (tile >= nM * nN) return;
+  const int per_group = GROUP_M * nN;
+  const int group = tile / per_group;
+  const int first_m = group * GROUP_M;
+  const int gsize = min(nM - first_m, GROUP_M);
+  const int in_g = tile - group * per_group;
+  const int m0 = (first_m + in_g % gsize) * BM;
+  const int n0 = (in_g / gsize) * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+  const int wm = wave >> 2, wn = wave & 3;
+  const int M = p.M, N = p.N, K = p.K;
+  const int KS = K / BK8;                    // k steps (K is a multiple of 128)
+
+  const int lrow8 = lane >> 3;
+  const int lunit = (lane & 7) ^ lrow8;
+  const char* a_base = (const char*)p.A + (size_t)m0 * p.lda;
+  const unsigned a_bytes = (unsigned)((size_t)(M - m0) * p.lda);
+  const unsigned a_step = (unsigned)(64 * p.lda);
+  const unsigned a_off0 = (unsigned)((wave * 8 + lrow8) * p.lda);
+  const char* b_base = (const char*)p.B + (size_t)n0 * p.ldb;
+  const unsigned b_bytes = (unsigned)((size_t)(N - n0) * p.ldb);
+  const unsigned b_step = (unsigned)(64 * p.ldb);
+  const unsigned b_off0 = (unsigned)((wave * 8 + lrow8) * p.ldb);
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t b_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_bytes, 0x00020000);
+  // scales: the 16-row groups of this wave's A rows and B rows; groups past
+  // the operand's padded rows load zero
+  const int ga0 = (m0 + wm * 128) >> 4, gb0 = (n0 + wn * WN) >> 4;
+  const __amdgpu_buffer_rsrc_t sa_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.a_scale, (short)0, (int)(((M + 15) >> 4) * KS * 64), 0x00020000);
+  const __amdgpu_buffer_rsrc_t sb_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.b_scale, (short)0, (int)(((N + 15) >> 4) * KS * 64), 0x00020000);
+
+  int sx0[8], sw0[NTW], sx1[8], sw1[NTW];
+  auto issue = [&](int kt, u32x4_t* As_s, u32x4_t* Bs_s, int (&sx)[8], int (&sw)[NTW])
+      __attribute__((always_inline)) {
+    const unsigned koff = (unsigned)(kt * BK8 + lunit * 16);
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(j * 8 + wave) * 64]), 16,
+                                               a_off0 + j * a_step + koff, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dma_dst(&Bs_s[(j * 8 + wave) * 64]), 16,
+                                               b_off0 + j * b_step + koff, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      sx[i] = __builtin_amdgcn_raw_buffer_load_b8(sa_rsrc, ((ga0 + i) * KS + kt) * 64 + lane, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+      sw[j] = __builtin_amdgcn_raw_buffer_load_b8(sb_rsrc, ((gb0 + j) * KS + kt) * 64 + lane, 0, 0);
+  };
+
+  f32x4_t acc[NTW][8];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int lrow = lane & 15;
+  const int g = lane >> 4;
+  auto step = [&](int kt, const u32x4_t* As_s, const u32x4_t* Bs_s, u32x4_t* As_n, u32x4_t* Bs_n,
+                  const int (&sx)[8], const int (&sw)[NTW], int (&sxn)[8], int (&swn)[NTW])
+      __attribute__((always_inline)) {
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 1 < KS) issue(kt + 1, As_n, Bs_n, sxn, swn);
+    i32x8_t wb[NTW];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int r = wn * WN + 16 * j + lrow;
+      wb[j] = units_to_i32x8(Bs_s[r * KU + swz(g, r)], Bs_s[r * KU + swz(g + 4, r)]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = wm * 128 + 16 * i + lrow;
+      const i32x8_t xa = units_to_i32x8(As_s[r * KU + swz(g, r)], As_s[r * KU + swz(g + 4, r)]);
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb[j], xa, acc[j][i], 0, 0, 0,
+                                                                     sw[j], 0, sx[i]);
+    }
+  };
+
+  issue(0, As0, Bs0, sx0, sw0);
+  for (int kt = 0; kt < KS; kt += 2) {
+    step(kt, As0, Bs0, As1, Bs1, sx0, sw0, sx1, sw1);
+    if (kt + 1 < KS) step(kt + 1, As1, Bs1, As0, Bs0, sx1, sw1, sx0, sw0);
+  }
+
+  staged_epilogue<BN, WN, NT8, EPI>(p, m0, n0, wm, wn, tid, acc, As0, As1, Bs0, Bs1);
+}
+
+template <int BN, int EPI>
+hipError_t run8_f8(const GemmArgs& a, hipStream_t s) {
+  const int nM = (a.M + BM - 1) / BM;
+  const int nN = (a.N + BN - 1) / BN;
+  const int tiles = nM * nN;
+  const int per_xcd = (tiles + 7) / 8;
+  hipLaunchKernelGGL((gemm8w_f8_kernel<BN, EPI>), dim3(8 * per_xcd), dim3(512), 0, s, a, nM, nN,
+                     per_xcd);
+  return hipGetLastError();
+}
+
 template <int BN, int AMODE, int EPI>
 hipError_t run8(const GemmArgs& a, hipStream_t s) {
   const int nM = (a.M + BM - 1) / BM;
@@ -628,6 +803,7 @@ hipError_t dispatch(const GemmArgs& a, int amode, int epi, hipStream_t s) {
       case EPI_STORE_GELU: return run_any<BN, A_PLAIN, EPI_STORE_GELU>(a, s);
       case EPI_RESID: return run_any<BN, A_PLAIN, EPI_RESID>(a, s);
       case EPI_STORE_F32: return run_any<BN, A_PLAIN, EPI_STORE_F32>(a, s);
+      case EPI_GELU_MX: return run_any<BN, A_PLAIN, EPI_GELU_MX>(a, s);
       default: break;
     }
   } else if (amode == A_CONV && epi == EPI_STORE_GELU) {
@@ -664,15 +840,37 @@ int pick_bn(int M, int N) {
   return best;
 }
 
+// the epilogue copies 16-byte chunks (or, for MX output, 32-value blocks) of
+// output rows
+bool epilogue_fits(const GemmArgs& a, int epi) {
+  if ((size_t)a.out & 15) return false;
+  if (epi == EPI_GELU_MX) return a.N % 128 == 0 && a.ldo % 16 == 0 && a.out_scale != nullptr;
+  const int epc = (epi == EPI_STORE || epi == EPI_STORE_GELU) ? 8 : 4;
+  return a.N % epc == 0 && a.ldo % epc == 0;
+}
+
 }  // namespace
 
 int g_gemm256_force_bn = 0;  // tuning hook: 0 = automatic
 
+hipError_t launch_gemm_f8(const GemmArgs& a, int epi, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.K <= 0 || a.K % 128 || a.lda % 16 || a.ldb % 16 || !a.a_scale || !a.b_scale ||
+      ((size_t)a.A & 15) || ((size_t)a.B & 15) || !epilogue_fits(a, epi))
+    return hipErrorInvalidValue;
+  switch (epi) {
+    case EPI_STORE: return run8_f8<256, EPI_STORE>(a, s);
+    case EPI_STORE_GELU: return run8_f8<256, EPI_STORE_GELU>(a, s);
+    case EPI_RESID: return run8_f8<256, EPI_RESID>(a, s);
+    case EPI_STORE_F32: return run8_f8<256, EPI_STORE_F32>(a, s);
+    case EPI_GELU_MX: return run8_f8<256, EPI_GELU_MX>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_gemm256(const GemmArgs& a, int amode, int epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  // the epilogue copies 16-byte chunks of output rows
-  const int epc = (epi == EPI_STORE || epi == EPI_STORE_GELU) ? 8 : 4;
-  if (a.N % epc || a.ldo % epc || ((size_t)a.out & 15)) return hipErrorInvalidValue;
+  if (!epilogue_fits(a, epi)) return hipErrorInvalidValue;
   const int bn = g_gemm256_force_bn ? g_gemm256_force_bn : pick_bn(a.M, a.N);
   switch (bn) {
     case 320: return dispatch<320>(a, amode, epi, s);

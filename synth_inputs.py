@@ -192,14 +192,14 @@ def round_to_bf16(a: np.ndarray) -> np.ndarray:
 def params(cfg: dict, seed: int, std: float = 0.02) -> dict[str, np.ndarray]:
     """Synthetic parameters: weights and biases ~ N(0, std); LayerNorm gain
     1 + N(0, std), LayerNorm shift ~ N(0, std).  float32, bf16-representable
-    when the workload's dtype is bf16."""
+    when the workload's dtype is bf16 or fp8 (whose other operands are bf16)."""
     rng = np.random.default_rng([seed, 2])
     out = {}
     for name, shape in param_shapes(cfg):
         a = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)
         if name.endswith("_g"):
             a = a + np.float32(1.0)
-        if cfg.get("dtype") == "bf16":
+        if cfg.get("dtype") in ("bf16", "fp8"):
             a = round_to_bf16(a)
         out[name] = a.astype(np.float32, copy=False)
     return out

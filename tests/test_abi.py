@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = aut.lib()
     names = declared_functions()
-    assert len(names) == len(aut.SIGNATURES) == 26
+    assert len(names) == len(aut.SIGNATURES) == 29
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(aut.SIGNATURES), "binding and header disagree"
@@ -224,3 +224,68 @@ def test_inject_argument_checks_before_launch():
     assert lib.aut_inject_audio(ok_ptr, ok_ptr, 4, 2046, ok_ptr, 10, 0, None) == 1  # dim % 4
     assert lib.aut_inject_audio(ok_ptr, ok_ptr, -1, 2048, ok_ptr, 10, 0, None) == 1
     assert lib.aut_inject_audio(ok_ptr, ok_ptr, 4, 2048, ok_ptr, 10, 7, None) == 1  # dtype
+
+
+# ---------------------------------------------------------------------------
+# MX-fp8 (AUT_FP8): sizes and argument checks, host only
+# ---------------------------------------------------------------------------
+
+
+def test_fp8_config_default_and_range():
+    c = aut.config()
+    assert c.fp8_gemms == aut.FP8_ALL == 31
+    aut.config_check(aut.config(fp8_gemms=0))
+    with pytest.raises(aut.AutError) as e:
+        aut.config_check(aut.config(fp8_gemms=32))
+    assert e.value.status == 1
+
+
+def test_mx_scale_bytes():
+    for rows, K in [(1, 128), (16, 128), (17, 1280), (14673, 5120), (0, 256)]:
+        assert aut.mx_scale_bytes(rows, K) == (rows + 15) // 16 * 16 * K // 32
+    for K in (0, 64, 1000):
+        with pytest.raises(aut.AutError):
+            aut.mx_scale_bytes(16, K)
+
+
+def test_fp8_weight_bytes_follow_the_mask():
+    cfg_d = si.model_config("wide")
+    d, F, O = cfg_d["d_model"], cfg_d["encoder_ffn_dim"], cfg_d["output_dim"]
+    L = cfg_d["encoder_layers"]
+    bf = aut.weights_bytes(aut.config(cfg_d), "bf16")
+    full = aut.weights_bytes(aut.config(cfg_d, fp8_gemms=aut.FP8_ALL), "fp8")
+    none = aut.weights_bytes(aut.config(cfg_d, fp8_gemms=0), "fp8")
+    assert none == bf
+    # each fp8 weight: 1 byte + 1/32 of a scale byte per element instead of 2 bytes
+    per_layer = 3 * d * d + d * d + 2 * F * d
+    elems = L * per_layer + d * d + O * d
+    saved = bf - full
+    assert abs(saved - elems * (1 - 1 / 32)) < 256 * (6 * L + 4)   # up to 256-byte alignment per array
+
+
+def test_fp8_needs_128_multiples():
+    cfg_d = dict(si.model_config("tiny"))
+    cfg_d.update(d_model=192, encoder_attention_heads=3)
+    with pytest.raises(aut.AutError) as e:
+        aut.weights_bytes(aut.config(cfg_d), "fp8")
+    assert e.value.status == 2
+    aut.weights_bytes(aut.config(cfg_d), "bf16")
+
+
+def test_mx_primitive_argument_checks():
+    L = aut.lib()
+    assert L.aut_mx_quantize(None, 4, 100, None, None, None) == 1
+    assert L.aut_mx_quantize(None, 0, 128, None, None, None) == 0      # nothing to do
+    assert L.aut_mx_matmul(None, None, 4, None, None, 6, 128, None, None) == 2   # N % 4
+    assert L.aut_mx_matmul(None, None, 4, None, None, 8, 96, None, None) == 1    # K % 128
+    assert L.aut_mx_matmul(None, None, 4, None, None, 8, 128, None, None) == 1   # NULL
+
+
+def test_mx_scale_layout_reindex():
+    # the binding's reindexing matches the documented formula, entry by entry
+    rows, K = 37, 256
+    flat = np.arange(aut.mx_scale_bytes(rows, K)) % 251
+    rm = aut.mx_scales_rowmajor(flat, rows, K)
+    for r in (0, 15, 16, 36):
+        for kb in range(K // 32):
+            assert rm[r, kb] == flat[((r // 16) * (K // 128) + kb // 4) * 64 + (kb % 4) * 16 + r % 16]

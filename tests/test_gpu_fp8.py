@@ -1,0 +1,189 @@
+"""GPU parity of the MX-fp8 products (AUT_FP8) through the C ABI.
+
+* The conversion (aut_mx_quantize, the same device code the LayerNorm,
+  attention and GELU-epilogue producers use): bit-exact codes and scale codes
+  against the oracle's ``mx_quantize`` on the same fp32 values.
+* One product (aut_mx_matmul): against the float64 product of the oracle's
+  dequantized operands, relative to sum |a| |b| (products of e4m3 values and
+  power-of-two scales are exact; what remains is the fp32 accumulation).
+* The encoder under AUT_FP8: against the oracle with the same products
+  quantized (``forward(..., fp8=mask)``), and against the unquantized oracle,
+  where the pages' acceptance criterion for 8-bit variants (per-token cosine
+  similarity > 0.999) is checked for the masks that meet it and the cost of
+  the others is reported.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth_inputs as si
+from gpu_common import features_dev, forward, sample_windows, small_cfg, token_cos, torch_mod, workload
+
+pytestmark = pytest.mark.gpu
+
+# aut_mx_matmul: max |gpu - ref| / (|A| |B|^T) entrywise.  The products of
+# e4m3 codes and power-of-two scales are exact; the error is the fp32
+# accumulation (K / 128 accumulating instructions of 128 products each),
+# measured below 1e-5 of sum |a| |b|.
+MX_MATMUL_TOL = 5e-5
+# Encoder under AUT_FP8 against the oracle with the same products quantized.
+# The two decide each e4m3 code from slightly different values (the GPU's
+# other operands are bf16 and its sums fp32), so near a rounding boundary
+# they pick neighbouring codes: two partly independent realizations of the
+# same quantization noise.  Per token, 1 - cos(gpu, fp8 oracle) must stay
+# within twice the quantization's own 1 - cos(fp8 oracle, unquantized oracle)
+# (the two realizations fully independent) plus the bf16 path's own 2e-5.
+FP8_NOISE_FACTOR = 2.0
+FP8_BF16_SLACK = 2e-5
+# the pages' criterion for an 8-bit variant: cosine similarity to the
+# full-precision encoder > 0.999, read as the mean over tokens
+PAGE_COS = 0.999
+
+
+def mx_inputs(R, K, seed):
+    """fp32 rows with the cases the conversion has: wide dynamic range across
+    rows, blocks whose first value dwarfs the rest (subnormal e4m3 codes),
+    all-zero blocks, block maxima exactly on and just above a scale boundary."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((R, K)) * np.exp2(rng.integers(-12, 12, (R, 1)))
+    if R > 3:
+        x[1] = rng.standard_normal(K) * 2.0 ** -14
+        x[1, ::32] = 1.0
+        x[2, :64] = 0.0
+        x[3, :32] = rng.uniform(-1, 1, 32) * 448.0 * 2.0 ** -5
+        x[3, 0] = 448.0 * 2.0 ** -5
+        x[3, 32:64] = rng.uniform(-1, 1, 32) * 448.0 * 2.0 ** -5
+        x[3, 32] = np.nextafter(np.float32(448.0 * 2.0 ** -5), np.float32(1e9))
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("R,K", [(1, 128), (37, 256), (1000, 1280), (300, 5120)])
+def test_mx_quantize_bit_exact(R, K):
+    from packed_windowed_attention_amd import aut
+    torch = torch_mod()
+    print(f"case: mx_quantize R={R} K={K}", flush=True)
+    x = mx_inputs(R, K, seed=R + K)
+    codes, scales = aut.mx_quantize(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    rc, rs = oracle.mx_quantize(x.astype(np.float64))
+    got_c = codes.cpu().numpy()
+    s = scales.cpu().numpy()
+    nbad = int(np.count_nonzero(got_c != rc))
+    print(f"[mx_quantize {R}x{K}] code mismatches {nbad}", flush=True)
+    assert nbad == 0
+    assert np.array_equal(aut.mx_scales_rowmajor(s, R, K), rs)
+    R16 = (R + 15) // 16 * 16
+    assert (aut.mx_scales_rowmajor(s, R16, K)[R:] == 0).all()   # padding rows: scale code 0
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 128), (300, 1280, 1280), (777, 100, 5120),
+                                   (2048, 2048, 1280), (4099, 3840, 1280)])
+def test_mx_matmul_vs_oracle(M, N, K):
+    from packed_windowed_attention_amd import aut
+    torch = torch_mod()
+    print(f"case: mx_matmul M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M * 7 + N)
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    b = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    ac, asc = aut.mx_quantize(torch.from_numpy(a).cuda())
+    bc, bsc = aut.mx_quantize(torch.from_numpy(b).cuda())
+    out = aut.mx_matmul(ac, asc, bc, bsc)
+    torch.cuda.synchronize()
+    qa = oracle.mx_round(a.astype(np.float64))
+    qb = oracle.mx_round(b.astype(np.float64))
+    assert np.array_equal(ac.cpu().numpy(), oracle.mx_quantize(a.astype(np.float64))[0])
+    ref = qa @ qb.T
+    bound = np.abs(qa) @ np.abs(qb).T
+    g = out.double().cpu().numpy()
+    err = np.abs(g - ref) / np.maximum(bound, 1e-30)
+    print(f"[mx_matmul {M}x{N}x{K}] max err/sum|ab| {err.max():.3e} median {np.median(err):.3e} "
+          f"normwise {np.abs(g - ref).max() / np.abs(ref).max():.3e}", flush=True)
+    assert np.isfinite(g).all()
+    assert err.max() <= MX_MATMUL_TOL
+
+
+def fp8_case(mask, layers=2):
+    cfg = small_cfg("fp8", encoder_layers=layers, fp8_gemms=mask)
+    lens = np.array([250, 0, 800, 37, 1737, 5, 100, 101])
+    feats = si.mel_features(lens, seed=31)
+    P = si.params(cfg, seed=31, std=0.05)
+    return cfg, lens, feats, P
+
+
+def report(g, ref, what):
+    cos = token_cos(g, ref)
+    mx = float(np.abs(g - ref).max())
+    print(f"[{what}] min cos {cos.min():.6f} mean cos {cos.mean():.6f} max-abs {mx:.3e} "
+          f"(ref max {np.abs(ref).max():.3f})", flush=True)
+    assert np.isfinite(g).all()
+    return cos
+
+
+def check_fp8(g, ref_q, ref, what):
+    """GPU against the fp8 oracle within the noise bound above; returns the
+    per-token cosine against the unquantized oracle."""
+    cq = report(g, ref_q, f"{what} vs fp8 oracle")
+    cr = report(g, ref, f"{what} vs unquantized oracle")
+    fmt = 1.0 - token_cos(ref_q, ref)
+    dev = 1.0 - cq
+    print(f"[{what}] quantization 1-cos: mean {fmt.mean():.2e}; gpu vs fp8 oracle / quantization: "
+          f"max {np.max(dev / np.maximum(fmt, 1e-12)):.2f}", flush=True)
+    assert np.all(dev <= FP8_NOISE_FACTOR * fmt + FP8_BF16_SLACK), what
+    return cr
+
+
+@pytest.mark.parametrize("mask", [1, 2, 4, 8, 16, 31])
+def test_small_fp8_masks(mask):
+    """Each product class alone and all of them, small ragged configuration."""
+    cfg_d, lens, feats, P = fp8_case(mask)
+    print(f"case: small fp8 mask {mask}", flush=True)
+    y, _ = forward(cfg_d, lens, feats, P)
+    ref_q, _ = oracle.forward(feats, lens, P, cfg_d, fp8=mask)
+    ref, _ = oracle.forward(feats, lens, P, cfg_d)
+    check_fp8(y, ref_q, ref, f"small mask {mask}")
+
+
+def test_fp8_mask_zero_is_bf16_bitwise():
+    """AUT_FP8 with no product selected runs exactly the bf16 path."""
+    cfg_d, lens, feats, P = fp8_case(0)
+    y8, _ = forward(cfg_d, lens, feats, P)
+    yb, _ = forward(dict(cfg_d, dtype="bf16"), lens, feats, P)
+    assert np.array_equal(y8, yb)
+
+
+def test_rag_fp8():
+    """4 ragged requests, 18 layers d 1024, all products MX-fp8: whole output."""
+    cfg_d, lens, feats, P = workload("rag")
+    cfg_d = dict(cfg_d, dtype="fp8", fp8_gemms=31)
+    print("case: rag fp8 (all products)", flush=True)
+    y, _ = forward(cfg_d, lens, feats, P)
+    ref_q, _ = oracle.forward(feats, lens, P, cfg_d, fp8=31)
+    ref, _ = oracle.forward(feats, lens, P, cfg_d)
+    check_fp8(y, ref_q, ref, "rag fp8")
+
+
+@pytest.mark.parametrize("mask", [31, 1])
+def test_wide_fp8_sampled_windows(mask):
+    """Full-width workload (24 layers, d 1280) under AUT_FP8, sampled windows.
+    mask 1 (the q/k/v projection only) meets the pages' cosine > 0.999 (mean
+    over tokens) against the unquantized encoder; every product on MX-fp8 does
+    not (e4m3 keeps 3 mantissa bits: about 7e-4 of cosine per product) and is
+    reported."""
+    cfg_d, lens, feats, P = workload("wide")
+    cfg_d = dict(cfg_d, dtype="fp8", fp8_gemms=mask)
+    print(f"case: wide fp8 mask {mask}, sampled windows", flush=True)
+    y, pl = forward(cfg_d, lens, feats, P)
+    opl = oracle.plan(lens, cfg_d)
+    assert pl.copy()[1] == opl["cu_seqlens"]
+    wins = sample_windows(opl, seed=si.workload_seed("wide") + 3, n_random=1)
+    res_q = oracle.forward_windows(feats, lens, P, cfg_d, wins, fp8=mask)
+    res = oracle.forward_windows(feats, lens, P, cfg_d, wins)
+    cos = []
+    for w in wins:
+        r0, ref_q = res_q[w]
+        g = y[r0:r0 + ref_q.shape[0]]
+        cos.append(check_fp8(g, ref_q, res[w][1], f"wide mask {mask} window {w}"))
+    cos = np.concatenate(cos)
+    print(f"[wide mask {mask}] vs unquantized: mean cos {cos.mean():.6f} min {cos.min():.6f}", flush=True)
+    if mask == 1:
+        assert cos.mean() > PAGE_COS

@@ -378,6 +378,15 @@ def torch_mx_round(x, block=32):
     return out.reshape(x.shape)
 
 
+def check_e4m3_round():
+    """the direct rounding against the code table, value by value"""
+    r = np.random.default_rng(12)
+    x = r.uniform(-1, 1, 50000) * np.exp2(r.integers(-14, 9, 50000))
+    vals = ao.e4m3_decode(np.arange(127))
+    x = np.concatenate([x[np.abs(x) <= 448], (vals[1:] + vals[:-1]) / 2, -vals, [0.0]])
+    return float(np.abs(ao.e4m3_round(x) - ao.e4m3_decode(ao.e4m3_encode(x))).max())
+
+
 def check_e4m3():
     r = np.random.default_rng(5)
     x = (r.uniform(-1, 1, 20000) * np.exp2(r.integers(-12, 9, 20000))).astype(np.float32)
@@ -399,12 +408,17 @@ def check_mx():
     x[7:12] = r.standard_normal((5, 128)) * 2.0 ** -14
     x[7:12, ::32] = 1.0
     x = x.astype(np.float32).astype(np.float64)
-    try:
-        got = ao.mx_round(x)
-    except ValueError:                          # an element past the e4m3 range
-        return float("inf")
-    d = np.abs(got - torch_mx_round(x)).reshape(-1, 32)
-    return float((d / np.abs(x).reshape(-1, 32).max(1, keepdims=True).clip(1e-300)).max())
+    ref = torch_mx_round(x)
+    worst = 0.0
+    # the value path (mx_round) and the code path (quantize, then dequantize)
+    for f in (ao.mx_round, lambda v: ao.mx_dequantize(*ao.mx_quantize(v))):
+        try:
+            got = f(x)
+        except ValueError:                      # an element past the e4m3 range
+            return float("inf")
+        d = np.abs(got - ref).reshape(-1, 32)
+        worst = max(worst, float((d / np.abs(x).reshape(-1, 32).max(1, keepdims=True).clip(1e-300)).max()))
+    return worst
 
 
 def check_linear_mx():
@@ -442,10 +456,26 @@ MUTATIONS = {
     "e4m3 truncated": ("e4m3_encode", lambda orig: _e4m3_trunc, check_e4m3),
     "e4m3 ties away from zero": ("e4m3_encode", lambda orig: (lambda x: orig(np.clip(np.asarray(x, dtype=np.float64) * (1 + 2.0 ** -40), -448, 448))), check_e4m3),
     "mx block of 16": ("MX_BLOCK", lambda orig: 16, check_mx),
+    "e4m3 round half up": ("e4m3_round", lambda orig: (lambda x: _e4m3_round_half_up(x)), check_e4m3_round),
+    "e4m3 round no subnormal floor": ("e4m3_round", lambda orig: _e4m3_round_no_subnormal, check_mx),
     "mx floor exponent rule": ("mx_block_exponent", lambda orig: (lambda a: np.where(np.asarray(a) > 0, np.floor(np.log2(np.where(np.asarray(a) > 0, a, 1.0))) - 8, -127).astype(np.int64)), check_mx),
     "mx scale bias 128": ("mx_dequantize", lambda orig: (lambda c, sc: orig(c, np.asarray(sc, dtype=np.int64) - 1)), check_mx),
     "mx weights left unquantized": ("linear_mx", lambda orig: (lambda x, w, b=None: ao.linear(ao.mx_round(x), w, b)), check_linear_mx),
 }
+
+
+def _e4m3_round_half_up(x):
+    x = np.asarray(x, dtype=np.float64)
+    _, E = np.frexp(x)
+    q = np.maximum(E - 1, -6) - 3
+    return np.sign(x) * np.ldexp(np.floor(np.ldexp(np.abs(x), -q) + 0.5), q)
+
+
+def _e4m3_round_no_subnormal(x):
+    x = np.asarray(x, dtype=np.float64)
+    _, E = np.frexp(x)
+    q = E - 1 - 3
+    return np.ldexp(np.rint(np.ldexp(x, -q)), q)
 
 
 def _e4m3_trunc(x):
@@ -648,6 +678,10 @@ def test_e4m3_decode_all_codes():
 
 def test_e4m3_encode_vs_torch():
     assert check_e4m3() == 0
+
+
+def test_e4m3_round_equals_code_table():
+    assert check_e4m3_round() == 0
 
 
 def test_e4m3_ties_to_even():
