@@ -638,8 +638,9 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
 // row l % 16 and the bytes of k in [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g
 // + 16), g = l / 16 (row units g and g + 4), and the scale byte of row l % 16,
 // block g of the step.  The scales of a step are 64 consecutive bytes per
-// 16-row group (mx_scale_index), one byte load per lane per fragment, issued
-// with the step's tile loads.
+// 16-row group (mx_scale_index); they travel with the step's tiles, straight
+// into LDS (one 256-byte load per four groups), and each lane reads its byte
+// there: no scale registers live across steps.
 template <int BN, int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
@@ -651,9 +652,13 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   constexpr int A_LOADS = A_UNITS / NT8;
   constexpr int B_LOADS = B_UNITS / NT8;
   constexpr int BK8 = 128;                   // codes per row per k step
-  static_assert(B_UNITS % NT8 == 0, "whole B loads per thread");
+  constexpr int SA_Q = BM / 64;              // 256-byte scale loads per step: 4 groups each
+  constexpr int SB_Q = BN / 64;
+  static_assert(B_UNITS % NT8 == 0 && BN % 64 == 0, "whole loads per thread");
+  static_assert(SA_Q + SB_Q <= 16, "scale loads: at most two per wave");
   __shared__ u32x4_t As0[A_UNITS], As1[A_UNITS];
   __shared__ u32x4_t Bs0[B_UNITS], Bs1[B_UNITS];
+  __shared__ unsigned Sa0[BM], Sa1[BM], Sb0[BN], Sb1[BN];  // 64 bytes per 16 rows: 4 per row
 
   const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (tile >= nM * nN) return;
@@ -686,16 +691,19 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
       __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t b_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_bytes, 0x00020000);
-  // scales: the 16-row groups of this wave's A rows and B rows; groups past
-  // the operand's padded rows load zero
-  const int ga0 = (m0 + wm * 128) >> 4, gb0 = (n0 + wn * WN) >> 4;
+  // Scale loads: wave w < SA_Q takes A groups 4 w .. 4 w + 3 of the tile,
+  // waves SA_Q .. SA_Q + SB_Q - 1 (mod 8) the B groups; lane l fills bytes
+  // 4 (l % 16) .. + 3 of group l / 16 of its four.  Groups past the operand's
+  // padded rows load zero.
   const __amdgpu_buffer_rsrc_t sa_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.a_scale, (short)0, (int)(((M + 15) >> 4) * KS * 64), 0x00020000);
   const __amdgpu_buffer_rsrc_t sb_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.b_scale, (short)0, (int)(((N + 15) >> 4) * KS * 64), 0x00020000);
+  const int sq_a = wave;                          // A quad of this wave, if < SA_Q
+  const int sq_b0 = (wave - SA_Q) & 7;            // first B quad of this wave
+  const int sgrp = lane >> 4, sbyte = 4 * (lane & 15);
 
-  int sx0[8], sw0[NTW], sx1[8], sw1[NTW];
-  auto issue = [&](int kt, u32x4_t* As_s, u32x4_t* Bs_s, int (&sx)[8], int (&sw)[NTW])
+  auto issue = [&](int kt, u32x4_t* As_s, u32x4_t* Bs_s, unsigned* Sa_s, unsigned* Sb_s)
       __attribute__((always_inline)) {
     const unsigned koff = (unsigned)(kt * BK8 + lunit * 16);
 #pragma unroll
@@ -706,12 +714,22 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
     for (int j = 0; j < B_LOADS; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dma_dst(&Bs_s[(j * 8 + wave) * 64]), 16,
                                                b_off0 + j * b_step + koff, 0, 0, 0);
+    if (sq_a < SA_Q) {
+      const int grp = (m0 >> 4) + 4 * sq_a + sgrp;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          sa_rsrc, dma_dst((const u32x4_t*)&Sa_s[64 * sq_a]), 4,
+          (unsigned)((grp * KS + kt) * 64 + sbyte), 0, 0, 0);
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      sx[i] = __builtin_amdgcn_raw_buffer_load_b8(sa_rsrc, ((ga0 + i) * KS + kt) * 64 + lane, 0, 0);
-#pragma unroll
-    for (int j = 0; j < NTW; ++j)
-      sw[j] = __builtin_amdgcn_raw_buffer_load_b8(sb_rsrc, ((gb0 + j) * KS + kt) * 64 + lane, 0, 0);
+    for (int r = 0; r < 2; ++r) {
+      const int q = sq_b0 + 8 * r;
+      if (q < SB_Q) {
+        const int grp = (n0 >> 4) + 4 * q + sgrp;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            sb_rsrc, dma_dst((const u32x4_t*)&Sb_s[64 * q]), 4,
+            (unsigned)((grp * KS + kt) * 64 + sbyte), 0, 0, 0);
+      }
+    }
   };
 
   f32x4_t acc[NTW][8];
@@ -722,35 +740,40 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
 
   const int lrow = lane & 15;
   const int g = lane >> 4;
-  auto step = [&](int kt, const u32x4_t* As_s, const u32x4_t* Bs_s, u32x4_t* As_n, u32x4_t* Bs_n,
-                  const int (&sx)[8], const int (&sw)[NTW], int (&sxn)[8], int (&swn)[NTW])
+  auto step = [&](int kt, const u32x4_t* As_s, const u32x4_t* Bs_s, const unsigned* Sa_s,
+                  const unsigned* Sb_s, u32x4_t* As_n, u32x4_t* Bs_n, unsigned* Sa_n, unsigned* Sb_n)
       __attribute__((always_inline)) {
     wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + 1 < KS) issue(kt + 1, As_n, Bs_n, sxn, swn);
+    if (kt + 1 < KS) issue(kt + 1, As_n, Bs_n, Sa_n, Sb_n);
+    const uint8_t* sa = (const uint8_t*)Sa_s + wm * 512 + lane;   // group wm * 8 + i: byte 64 i
+    const uint8_t* sb = (const uint8_t*)Sb_s + wn * (WN * 4) + lane;
     i32x8_t wb[NTW];
+    int sw[NTW];
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
       const int r = wn * WN + 16 * j + lrow;
       wb[j] = units_to_i32x8(Bs_s[r * KU + swz(g, r)], Bs_s[r * KU + swz(g + 4, r)]);
+      sw[j] = sb[64 * j];
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = wm * 128 + 16 * i + lrow;
       const i32x8_t xa = units_to_i32x8(As_s[r * KU + swz(g, r)], As_s[r * KU + swz(g + 4, r)]);
+      const int sx = sa[64 * i];
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
         acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb[j], xa, acc[j][i], 0, 0, 0,
-                                                                     sw[j], 0, sx[i]);
+                                                                     sw[j], 0, sx);
     }
   };
 
-  issue(0, As0, Bs0, sx0, sw0);
+  issue(0, As0, Bs0, Sa0, Sb0);
   for (int kt = 0; kt < KS; kt += 2) {
-    step(kt, As0, Bs0, As1, Bs1, sx0, sw0, sx1, sw1);
-    if (kt + 1 < KS) step(kt + 1, As1, Bs1, As0, Bs0, sx1, sw1, sx0, sw0);
+    step(kt, As0, Bs0, Sa0, Sb0, As1, Bs1, Sa1, Sb1);
+    if (kt + 1 < KS) step(kt + 1, As1, Bs1, Sa1, Sb1, As0, Bs0, Sa0, Sb0);
   }
 
   staged_epilogue<BN, WN, NT8, EPI>(p, m0, n0, wm, wn, tid, acc, As0, As1, Bs0, Bs1);
@@ -853,19 +876,52 @@ bool epilogue_fits(const GemmArgs& a, int epi) {
 
 int g_gemm256_force_bn = 0;  // tuning hook: 0 = automatic
 
+namespace {
+
+template <int BN>
+hipError_t dispatch_f8(const GemmArgs& a, int epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: return run8_f8<BN, EPI_STORE>(a, s);
+    case EPI_STORE_GELU: return run8_f8<BN, EPI_STORE_GELU>(a, s);
+    case EPI_RESID: return run8_f8<BN, EPI_RESID>(a, s);
+    case EPI_STORE_F32: return run8_f8<BN, EPI_STORE_F32>(a, s);
+    case EPI_GELU_MX: return run8_f8<BN, EPI_GELU_MX>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// column tile of the fp8 kernel: 320 or 256, whichever fills the 256 CUs'
+// tile slots and the columns better (ties to 320, fewer operand bytes per flop)
+int pick_bn_f8(int M, int N) {
+  const int nM = (M + BM - 1) / BM;
+  int best = 320;
+  double best_eff = -1.0;
+  for (int bn : {320, 256}) {
+    const int nN = (N + bn - 1) / bn;
+    const long tiles = (long)nM * nN;
+    const long slots = ((tiles + 255) / 256) * 256;
+    const double eff = (double)tiles / (double)slots * (double)N / (double)(nN * bn);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = bn;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+int g_gemm_f8_force_bn = 0;  // tuning hook: 0 = automatic
+
 hipError_t launch_gemm_f8(const GemmArgs& a, int epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K <= 0 || a.K % 128 || a.lda % 16 || a.ldb % 16 || !a.a_scale || !a.b_scale ||
       ((size_t)a.A & 15) || ((size_t)a.B & 15) || !epilogue_fits(a, epi))
     return hipErrorInvalidValue;
-  switch (epi) {
-    case EPI_STORE: return run8_f8<256, EPI_STORE>(a, s);
-    case EPI_STORE_GELU: return run8_f8<256, EPI_STORE_GELU>(a, s);
-    case EPI_RESID: return run8_f8<256, EPI_RESID>(a, s);
-    case EPI_STORE_F32: return run8_f8<256, EPI_STORE_F32>(a, s);
-    case EPI_GELU_MX: return run8_f8<256, EPI_GELU_MX>(a, s);
-    default: return hipErrorInvalidValue;
-  }
+  const int bn = g_gemm_f8_force_bn ? g_gemm_f8_force_bn : pick_bn_f8(a.M, a.N);
+  if (bn == 320) return dispatch_f8<320>(a, epi, s);
+  if (bn == 256) return dispatch_f8<256>(a, epi, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm256(const GemmArgs& a, int amode, int epi, hipStream_t s) {
