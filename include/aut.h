@@ -21,7 +21,9 @@
  *    pointers are ordinary host memory.  The caller owns every buffer
  *    (features, parameters, packed parameters, workspace, outputs) and the
  *    stream.  The library never allocates or frees device memory and never
- *    synchronises the device, except where a call says so.
+ *    synchronises the device, except where a call says so.  Host-to-device
+ *    copies of host arguments (plan tables, lengths) go through one pinned
+ *    host buffer per device that the library keeps (see aut_plan_upload).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *  - All argument checks happen before the first launch: a call that fails
  *    validation has enqueued nothing.
@@ -183,11 +185,14 @@ aut_status aut_weights_pack(const aut_config* cfg, const aut_weight_ptrs* src, a
 aut_status aut_workspace_bytes(const aut_config* cfg, const aut_plan_t* plan, aut_dtype dtype,
                                size_t* bytes);
 
-/* Copies the plan's tables into the workspace (asynchronous H2D on
- * `stream`).  The plan must not be destroyed before the stream has passed
- * this copy.  Must precede aut_encode_planned / aut_frontend / aut_encode_packed
- * with the same plan and workspace; it is the step kept outside a captured
- * graph (the m-star page builds the attention plan outside the graph). */
+/* Copies the plan's tables into the workspace: into a library-owned pinned
+ * host buffer (one per device, grown on demand, kept until the process ends),
+ * then one asynchronous H2D copy on `stream`.  The plan may be destroyed as
+ * soon as this returns.  Before reusing the pinned buffer the call waits, on
+ * the host, for the previous upload's copy out of it to finish.  Must precede
+ * aut_encode_planned / aut_frontend / aut_encode_packed with the same plan and
+ * workspace; it is the step kept outside a captured graph (the m-star page
+ * builds the attention plan outside the graph). */
 aut_status aut_plan_upload(const aut_plan_t* plan, void* workspace, size_t workspace_bytes,
                            void* stream);
 
@@ -199,8 +204,8 @@ aut_status aut_plan_upload(const aut_plan_t* plan, void* workspace, size_t works
  * packed: the aut_weights_pack buffer of the same cfg and dtype.
  * out: device fp32 [total_tokens, output_dim], packed row order.
  * workspace: device, >= aut_workspace_bytes for this batch.
- * Synchronises `stream` once, after the plan upload, so the temporary plan can
- * be freed; everything else is asynchronous. */
+ * Asynchronous on `stream`; the plan upload goes through aut_plan_upload's
+ * pinned buffer, so the temporary plan is freed before the call returns. */
 aut_status aut_encode(const aut_config* cfg, const float* features, int32_t T_max,
                       const int32_t* feature_lens, int32_t B, const void* packed, aut_dtype dtype,
                       float* out, void* workspace, size_t workspace_bytes, void* stream);
@@ -296,8 +301,8 @@ aut_status aut_logmel_workspace_bytes(int32_t B, size_t* bytes);
  * them, host int32, each 0 or > 200 and <= S_max); features: device fp32
  * [B, 128, T_max], T_max >= max(sample_lens) / 160 and a multiple of 4 for the
  * 16-byte stores; frames past a request's count are not written.  Copies the
- * lengths into the workspace and synchronises the stream once, like
- * aut_encode; the rest is asynchronous. */
+ * lengths into the workspace through the pinned buffer (sample_lens may be
+ * freed when the call returns); asynchronous on `stream`. */
 aut_status aut_logmel(const float* audio, int32_t S_max, const int32_t* sample_lens, int32_t B,
                       const void* tables, float* features, int32_t T_max, void* workspace,
                       size_t workspace_bytes, void* stream);

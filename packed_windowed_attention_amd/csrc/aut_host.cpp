@@ -568,6 +568,49 @@ extern "C" aut_status aut_workspace_bytes(const aut_config* cfg, const aut_plan_
   return AUT_OK;
 }
 
+namespace {
+
+// Pinned staging of plan uploads, one buffer per device.  A copy from
+// pageable host memory makes the calling thread wait until the stream has
+// drained (the runtime stages it synchronously), which leaves the GPU idle
+// between forwards; from pinned memory the copy is queued like a kernel.  The
+// event marks the end of the last copy out of the buffer: the host waits for
+// it before writing the buffer again (in steady state it has long passed).
+struct PlanStaging {
+  char* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+};
+std::mutex g_stage_mu;
+std::vector<PlanStaging> g_stage;
+
+// Host data -> device `dst` (bytes) through the device's pinned staging
+// buffer: `fill` writes the image into the buffer, then one queued copy.
+template <typename Fill>
+aut_status upload_pinned(void* dst, size_t bytes, hipStream_t s, Fill fill) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(g_stage_mu);
+  if ((int)g_stage.size() <= dev) g_stage.resize(dev + 1);
+  PlanStaging& st = g_stage[dev];
+  if (st.done) HIPCHK(hipEventSynchronize(st.done));
+  else HIPCHK(hipEventCreateWithFlags(&st.done, hipEventDisableTiming));
+  if (st.cap < bytes) {
+    if (st.host) HIPCHK(hipHostFree(st.host));
+    st.host = nullptr;
+    st.cap = 0;
+    const size_t cap = std::max<size_t>(align256(bytes + bytes / 4), (size_t)1 << 20);
+    HIPCHK(hipHostMalloc((void**)&st.host, cap, hipHostMallocDefault));
+    st.cap = cap;
+  }
+  fill(st.host);
+  HIPCHK(hipMemcpyAsync(dst, st.host, bytes, hipMemcpyHostToDevice, s));
+  HIPCHK(hipEventRecord(st.done, s));
+  return AUT_OK;
+}
+
+}  // namespace
+
 extern "C" aut_status aut_plan_upload(const aut_plan_t* plan, void* ws, size_t ws_bytes,
                                       void* stream) {
   if (!plan) return fail(AUT_ERR_INVALID_ARG, "plan is NULL");
@@ -576,16 +619,13 @@ extern "C" aut_status aut_plan_upload(const aut_plan_t* plan, void* ws, size_t w
   if (plan->total == 0) return AUT_OK;
   if (!ws) return fail(AUT_ERR_INVALID_ARG, "workspace is NULL");
   if (ws_bytes < need) return fail(AUT_ERR_WORKSPACE_TOO_SMALL, "workspace too small for the plan");
-  hipStream_t s = (hipStream_t)stream;
-  char* b = (char*)ws;
-  HIPCHK(hipMemcpyAsync(b + W.chunks, plan->chunks.data(), plan->chunks.size() * sizeof(aut_chunk),
-                        hipMemcpyHostToDevice, s));
-  HIPCHK(hipMemcpyAsync(b + W.rowmap, plan->rowmap.data(), plan->rowmap.size() * 4,
-                        hipMemcpyHostToDevice, s));
-  HIPCHK(hipMemcpyAsync(b + W.cu, plan->cu.data(), plan->cu.size() * 4, hipMemcpyHostToDevice, s));
-  HIPCHK(hipMemcpyAsync(b + W.worder, plan->worder.data(), plan->worder.size() * 4,
-                        hipMemcpyHostToDevice, s));
-  return AUT_OK;
+  // the four tables are consecutive pieces of the workspace: one image, one copy
+  return upload_pinned((char*)ws + W.chunks, need - W.chunks, (hipStream_t)stream, [&](char* h) {
+    memcpy(h, plan->chunks.data(), plan->chunks.size() * sizeof(aut_chunk));
+    memcpy(h + (W.rowmap - W.chunks), plan->rowmap.data(), plan->rowmap.size() * 4);
+    memcpy(h + (W.cu - W.chunks), plan->cu.data(), plan->cu.size() * 4);
+    memcpy(h + (W.worder - W.chunks), plan->worder.data(), plan->worder.size() * 4);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -872,12 +912,8 @@ extern "C" aut_status aut_encode(const aut_config* cfg, const float* features, i
   st = check_common(cfg, plan, dt, packed, ws, ws_bytes, &W);
   if (st == AUT_OK) st = check_features(features, T_max, *plan);
   if (st == AUT_OK && plan->total > 0 && !out) st = fail(AUT_ERR_INVALID_ARG, "out is NULL");
+  // the upload copies the tables out of the plan before it returns
   if (st == AUT_OK) st = aut_plan_upload(plan, ws, ws_bytes, stream);
-  if (st == AUT_OK && plan->total > 0) {
-    // the copies read the plan's host memory: let them finish before it is freed
-    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
-    if (e != hipSuccess) st = fail(AUT_ERR_HIP, "hipStreamSynchronize failed: %s", hipGetErrorString(e));
-  }
   if (st == AUT_OK)
     st = aut_encode_planned(cfg, plan, features, T_max, packed, dt, out, ws, ws_bytes, stream);
   aut_plan_destroy(plan);
@@ -1015,11 +1051,12 @@ extern "C" aut_status aut_logmel(const float* audio, int32_t S_max, const int32_
   hipStream_t s = (hipStream_t)stream;
   int* lens_dev = (int*)ws;
   unsigned* mx = (unsigned*)((char*)ws + align256((size_t)B * 4));
-  hipError_t e = hipMemcpyAsync(lens_dev, sample_lens, (size_t)B * 4, hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);  // the host lengths may go away after the call
-  if (e != hipSuccess) return fail(AUT_ERR_HIP, "length upload failed: %s", hipGetErrorString(e));
+  // the host lengths may go away after the call: copied out before it returns
+  aut_status ust = upload_pinned(lens_dev, (size_t)B * 4, s,
+                                 [&](char* h) { memcpy(h, sample_lens, (size_t)B * 4); });
+  if (ust != AUT_OK) return ust;
   aut::prof_begin(s);
-  e = aut::launch_logmel(audio, S_max, lens_dev, B, max_frames, (const float*)tables, features, T_max,
+  hipError_t e = aut::launch_logmel(audio, S_max, lens_dev, B, max_frames, (const float*)tables, features, T_max,
                          mx, s);
   if (e != hipSuccess) return fail(AUT_ERR_HIP, "log-mel launch failed: %s", hipGetErrorString(e));
   double frames = 0;
