@@ -230,8 +230,8 @@ def window_attention(q, k, v, cu_seqlens, num_heads: int) -> np.ndarray:
 
 E4M3_MAX = 448.0
 MX_BLOCK = 32
-FP8_QKV, FP8_OUT, FP8_FC1, FP8_FC2, FP8_PROJ = 1, 2, 4, 8, 16
-FP8_ALL = 31
+FP8_QKV, FP8_OUT, FP8_FC1, FP8_FC2, FP8_PROJ, FP8_CONV = 1, 2, 4, 8, 16, 32
+FP8_ALL = 63
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -324,6 +324,22 @@ def mx_round(x) -> np.ndarray:
 _MX_WEIGHTS: dict = {}
 
 
+def linear_conv_out_mx(u: np.ndarray, w: np.ndarray, b, F: int) -> np.ndarray:
+    """conv_out on MX-fp8 operands.  u holds the token features in the
+    channel-major flatten c * F + f; the contraction blocks are 32 consecutive
+    channels of one frequency bin (the GPU stores the stem output bin-major),
+    so both sides are rounded in the order f * C + c and put back."""
+    u = np.asarray(u, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    C = u.shape[1] // F
+    perm = (np.arange(C)[None, :] * F + np.arange(F)[:, None]).reshape(-1)   # f * C + c -> c * F + f
+    uq = np.empty_like(u)
+    uq[:, perm] = mx_round(u[:, perm])
+    wq = np.empty_like(w)
+    wq[:, perm] = mx_round(w[:, perm])
+    return linear(uq, wq, b)
+
+
 def _mx_weight(w) -> np.ndarray:
     """mx_round of a parameter array, remembered per array object (a
     parameter is rounded once however many windows or calls use it)."""
@@ -334,6 +350,28 @@ def _mx_weight(w) -> np.ndarray:
         hit = (w, mx_round(np.asarray(w, dtype=np.float64)))
         _MX_WEIGHTS[id(w)] = hit
     return hit[1]
+
+
+def conv2d_k3s2p1_mx(x: np.ndarray, w: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """``conv2d_k3s2p1`` as a product with MX-fp8 operands.  Its contraction
+    axis is (tap, input channel): for each of the nine taps the strided input
+    patch meets w[:, :, kh, kw] over the channels, so the blocks of 32 run over
+    consecutive channels of one tap (C_in a multiple of 32), on both sides."""
+    cin, H, W = x.shape
+    if cin % MX_BLOCK:
+        raise ValueError("conv2d_k3s2p1_mx: input channels must be a multiple of 32")
+    Ho, Wo = conv_out_len(H), conv_out_len(W)
+    xp = np.zeros((cin, H + 2, W + 2), dtype=np.float64)
+    xp[:, 1:H + 1, 1:W + 1] = x
+    out = np.zeros((w.shape[0], Ho, Wo), dtype=np.float64)
+    for kh in range(3):
+        for kw in range(3):
+            patch = xp[:, kh:kh + 2 * Ho:2, kw:kw + 2 * Wo:2]            # [Cin, Ho, Wo]
+            pq = mx_round(patch.reshape(cin, -1).T).T.reshape(patch.shape)
+            wq = mx_round(np.asarray(w[:, :, kh, kw], dtype=np.float64))  # [Cout, Cin]
+            out += np.tensordot(wq, pq, axes=(1, 0))
+    out += np.asarray(b, dtype=np.float64)[:, None, None]
+    return out
 
 
 def linear_mx(x: np.ndarray, w: np.ndarray, b=None) -> np.ndarray:
@@ -357,12 +395,14 @@ def chunk_image(features: np.ndarray, b: int, frame0: int, valid: int, cfg: dict
     return img
 
 
-def conv_stem(img: np.ndarray, P: dict) -> np.ndarray:
+def conv_stem(img: np.ndarray, P: dict, fp8: int = 0) -> np.ndarray:
     """Three Conv2d(k3, s2, p1) layers, each followed by GELU:
-    [1, 128, 100] -> [C, 16, 13]."""
+    [1, 128, 100] -> [C, 16, 13].  FP8_CONV: conv2 and conv3 (conv1 has one
+    input channel: no contraction to speak of) on MX-fp8 operands."""
+    conv = conv2d_k3s2p1_mx if fp8 & FP8_CONV else conv2d_k3s2p1
     a = gelu(conv2d_k3s2p1(img, P["conv1_w"], P["conv1_b"]))
-    a = gelu(conv2d_k3s2p1(a, P["conv2_w"], P["conv2_b"]))
-    a = gelu(conv2d_k3s2p1(a, P["conv3_w"], P["conv3_b"]))
+    a = gelu(conv(a, P["conv2_w"], P["conv2_b"]))
+    a = gelu(conv(a, P["conv3_w"], P["conv3_b"]))
     return a
 
 
@@ -374,10 +414,12 @@ def flatten_tokens(a3: np.ndarray, vt: int) -> np.ndarray:
     return a3[:, :, :vt].transpose(2, 0, 1).reshape(vt, C * Fq)
 
 
-def frontend(features, feature_lens, P: dict, cfg: dict, chunk_ids=None):
+def frontend(features, feature_lens, P: dict, cfg: dict, chunk_ids=None, fp8: int = 0):
     """m-star ``frontend``: chunk, pad, convolve, conv_out, add positions,
     keep the valid tokens.  Returns ([rows, d_model], the plan); ``chunk_ids``
-    restricts the work to some chunks (rows returned in chunk order)."""
+    restricts the work to some chunks (rows returned in chunk order).
+    FP8_CONV: conv2, conv3 and conv_out on MX-fp8 operands (conv_out's blocks
+    are 32 channels of one frequency bin, see ``linear_conv_out_mx``)."""
     pl = plan(feature_lens, cfg)
     d = cfg["d_model"]
     pe = sinusoid_table(cfg["max_source_positions"], d)
@@ -385,9 +427,12 @@ def frontend(features, feature_lens, P: dict, cfg: dict, chunk_ids=None):
     rows = []
     for ci in ids:
         b, f0, vf, vt, _ = pl["chunks"][ci]
-        a3 = conv_stem(chunk_image(features, b, f0, vf, cfg), P)       # [C, 16, 13]
+        a3 = conv_stem(chunk_image(features, b, f0, vf, cfg), P, fp8)  # [C, 16, 13]
         u = flatten_tokens(a3, vt)
-        e = linear(u, P["conv_out_w"], P.get("conv_out_b"))
+        if fp8 & FP8_CONV:
+            e = linear_conv_out_mx(u, P["conv_out_w"], P.get("conv_out_b"), a3.shape[1])
+        else:
+            e = linear(u, P["conv_out_w"], P.get("conv_out_b"))
         e = e + pe[:vt]
         rows.append(e)
     if rows:
@@ -430,7 +475,7 @@ def encode(hidden: np.ndarray, cu_seqlens, P: dict, cfg: dict, fp8: int = 0) -> 
 
 def forward(features, feature_lens, P: dict, cfg: dict, fp8: int = 0):
     """m-star ``forward``: (output [total_tokens, output_dim], layout)."""
-    hidden, pl = frontend(features, feature_lens, P, cfg)
+    hidden, pl = frontend(features, feature_lens, P, cfg, fp8=fp8)
     return encode(hidden, pl["cu_seqlens"], P, cfg, fp8), pl
 
 
@@ -463,7 +508,7 @@ def forward_windows(features, feature_lens, P: dict, cfg: dict, windows, fp8: in
     res = {}
     for w in windows:
         ids = wch[w]
-        hidden, _ = frontend(features, feature_lens, P, cfg, chunk_ids=ids)
+        hidden, _ = frontend(features, feature_lens, P, cfg, chunk_ids=ids, fp8=fp8)
         n = hidden.shape[0]
         res[w] = (pl["cu_seqlens"][w], encode(hidden, [0, n], P, cfg, fp8))
     return res

@@ -430,6 +430,52 @@ def check_linear_mx():
     return float(np.abs(ao.linear_mx(x, w, b) - ref).max())
 
 
+def check_conv_mx():
+    """conv2d_k3s2p1_mx against an explicit im2col product, k = tap * C + c,
+    rounded with the torch-built MX quantizer."""
+    r = np.random.default_rng(13)
+    x = r.standard_normal((64, 7, 6))
+    x[:16] *= 2.0 ** -16        # the blocks matter only where they mix magnitudes
+    x = x.astype(np.float32).astype(np.float64)
+    w = (r.standard_normal((5, 64, 3, 3)) * 0.1).astype(np.float32).astype(np.float64)
+    b = r.standard_normal(5)
+    Ho, Wo = 4, 3
+    xp = np.pad(x, ((0, 0), (1, 1), (1, 1)))
+    cols = np.zeros((Ho * Wo, 9 * 64))
+    for oy in range(Ho):
+        for ox in range(Wo):
+            for kh in range(3):
+                for kw in range(3):
+                    t = 3 * kh + kw
+                    cols[oy * Wo + ox, t * 64:(t + 1) * 64] = xp[:, 2 * oy + kh, 2 * ox + kw]
+    wm = np.zeros((5, 9 * 64))
+    for kh in range(3):
+        for kw in range(3):
+            t = 3 * kh + kw
+            wm[:, t * 64:(t + 1) * 64] = w[:, :, kh, kw]
+    ref = (torch_mx_round(cols) @ torch_mx_round(wm).T + b).T.reshape(5, Ho, Wo)
+    return float(np.abs(ao.conv2d_k3s2p1_mx(x, w, b) - ref).max())
+
+
+def check_conv_out_mx():
+    """conv_out on MX-fp8 against an explicit reorder to f * C + c."""
+    r = np.random.default_rng(14)
+    C, F = 64, 16
+    u = r.standard_normal((7, C * F))
+    u[:, 0::2] *= 2.0 ** -16    # even bins (index c * F + f, F even) tiny
+    u = u.astype(np.float32).astype(np.float64)
+    w = (r.standard_normal((9, C * F)) * 0.05).astype(np.float32).astype(np.float64)
+    b = r.standard_normal(9)
+    ub = np.zeros_like(u)
+    wb = np.zeros_like(w)
+    for f in range(F):
+        for c in range(C):
+            ub[:, f * C + c] = u[:, c * F + f]
+            wb[:, f * C + c] = w[:, c * F + f]
+    ref = torch_mx_round(ub) @ torch_mx_round(wb).T + b
+    return float(np.abs(ao.linear_conv_out_mx(u, w, b, F) - ref).max())
+
+
 MUTATIONS = {
     "conv kernel transposed": ("conv2d_k3s2p1", lambda orig: (lambda x, w, b: orig(x, np.swapaxes(w, 2, 3), b)), check_conv),
     "conv bias dropped": ("conv2d_k3s2p1", lambda orig: (lambda x, w, b: orig(x, w, np.zeros_like(b))), check_conv),
@@ -461,7 +507,20 @@ MUTATIONS = {
     "mx floor exponent rule": ("mx_block_exponent", lambda orig: (lambda a: np.where(np.asarray(a) > 0, np.floor(np.log2(np.where(np.asarray(a) > 0, a, 1.0))) - 8, -127).astype(np.int64)), check_mx),
     "mx scale bias 128": ("mx_dequantize", lambda orig: (lambda c, sc: orig(c, np.asarray(sc, dtype=np.int64) - 1)), check_mx),
     "mx weights left unquantized": ("linear_mx", lambda orig: (lambda x, w, b=None: ao.linear(ao.mx_round(x), w, b)), check_linear_mx),
+    "conv mx blocks across taps": ("conv2d_k3s2p1_mx", lambda orig: _conv_mx_c_major, check_conv_mx),
+    "conv_out mx channel-major blocks": ("linear_conv_out_mx", lambda orig: (lambda u, w, b, F: ao.linear_mx(u, w, b)), check_conv_out_mx),
 }
+
+
+def _conv_mx_c_major(x, w, b):
+    """planted: the contraction blocks taken in the channel-major order c * 9 + tap"""
+    cin, H, W = x.shape
+    Ho, Wo = ao.conv_out_len(H), ao.conv_out_len(W)
+    xp = np.pad(x, ((0, 0), (1, 1), (1, 1)))
+    cols = np.stack([xp[:, kh:kh + 2 * Ho:2, kw:kw + 2 * Wo:2] for kh in range(3) for kw in range(3)], 1)
+    cols = cols.reshape(cin * 9, Ho * Wo).T                    # k = c * 9 + tap
+    wm = w.reshape(w.shape[0], cin * 9)
+    return (ao.mx_round(cols) @ ao.mx_round(wm).T + b).T.reshape(-1, Ho, Wo)
 
 
 def _e4m3_round_half_up(x):
@@ -728,8 +787,16 @@ def test_linear_mx_vs_independent_build():
     assert check_linear_mx() < 1e-12
 
 
+def test_conv_mx_vs_im2col():
+    assert check_conv_mx() < 1e-12
+
+
+def test_conv_out_mx_vs_reorder():
+    assert check_conv_out_mx() < 1e-12
+
+
 def test_fp8_encoder_masks():
-    cfg = small_cfg(encoder_layers=1)
+    cfg = small_cfg(encoder_layers=1, downsample_hidden_size=32)
     lens = np.array([420], dtype=np.int32)
     feats = si.mel_features(lens, seed=3)
     P = si.params(cfg, seed=4)
@@ -737,7 +804,7 @@ def test_fp8_encoder_masks():
     same, _ = ao.forward(feats, lens, P, cfg, fp8=0)
     assert np.array_equal(base, same)
     cos_all = None
-    for bit in (ao.FP8_QKV, ao.FP8_OUT, ao.FP8_FC1, ao.FP8_FC2, ao.FP8_PROJ, ao.FP8_ALL):
+    for bit in (ao.FP8_QKV, ao.FP8_OUT, ao.FP8_FC1, ao.FP8_FC2, ao.FP8_PROJ, ao.FP8_CONV, ao.FP8_ALL):
         out, _ = ao.forward(feats, lens, P, cfg, fp8=bit)
         assert not np.array_equal(out, base)
         cos = (out * base).sum(1) / np.linalg.norm(out, axis=1) / np.linalg.norm(base, axis=1)
