@@ -249,6 +249,7 @@ def fp8_rate(aut, torch, cfg_d, P, fd, lens, steps, mask):
                    gemm_fp8_avg_us=1e3 * g8["total_ms"] / g8["launches"])
     if st["gemm"]["launches"]:
         res["gemm_bf16_ms_per_step"] = st["gemm"]["total_ms"] / steps
+    res["ms_per_step_by_class"] = {c: v["total_ms"] / steps for c, v in st.items() if v["launches"]}
     del ws, packed, out
     return res
 
@@ -460,9 +461,10 @@ def main():
         res["stream"] = stream_latency(aut, torch, cfg, packed, dtype, feats, args.stream_steps)
         log(f"stream: {res['stream']['step_ms_p50']:.3f} ms per 1 s append (p50)")
     if args.fp8_steps > 0 and dtype == "bf16":
-        # all encoder and projector products on MX-fp8, and the q/k/v
-        # projection alone (the mask that keeps the pages' cosine > 0.999)
-        res["fp8"] = [fp8_rate(aut, torch, cfg_d, P, fd, lens, args.fp8_steps, m) for m in (31, 1)]
+        # every product on MX-fp8 (conv stem, layers, projector), and the
+        # conv stem with the q/k/v projection (the mask that keeps the pages'
+        # cosine > 0.999)
+        res["fp8"] = [fp8_rate(aut, torch, cfg_d, P, fd, lens, args.fp8_steps, m) for m in (63, 33)]
         for r in res["fp8"]:
             log(f"fp8 mask {r['fp8_gemms']}: {r['ms_per_step']:.3f} ms/step, "
                 f"fp8 products {r.get('gemm_fp8_tflops', 0):.0f} TFLOP/s")

@@ -74,7 +74,10 @@ enum {
   AUT_FP8_FC1 = 4,   /* FFN fc1 (operand: LayerNorm 2 output) */
   AUT_FP8_FC2 = 8,   /* FFN fc2 (operand: GELU(fc1) output) */
   AUT_FP8_PROJ = 16, /* projector proj1 and proj2 */
-  AUT_FP8_ALL = 31
+  AUT_FP8_CONV = 32, /* conv stem: conv2, conv3 (blocks of 32 channels of one tap) and conv_out
+                        (32 channels of one frequency bin); needs downsample_hidden_size a
+                        multiple of 32 */
+  AUT_FP8_ALL = 63
 };
 
 /* Model hyper-parameters.  Field names and defaults follow AuTEncoderConfig

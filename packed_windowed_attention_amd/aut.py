@@ -20,8 +20,8 @@ DTYPES = {"fp32": 0, "bf16": 1, "fp8": 2}
 KERNEL_CLASSES = ["conv1", "conv_gemm", "conv_out", "layernorm", "gemm", "attention", "logmel",
                   "gemm_fp8"]
 # aut_config.fp8_gemms bits (the products on MX-fp8 operands under "fp8")
-FP8_QKV, FP8_OUT, FP8_FC1, FP8_FC2, FP8_PROJ = 1, 2, 4, 8, 16
-FP8_ALL = 31
+FP8_QKV, FP8_OUT, FP8_FC1, FP8_FC2, FP8_PROJ, FP8_CONV = 1, 2, 4, 8, 16, 32
+FP8_ALL = 63
 
 CONFIG_FIELDS = ["d_model", "encoder_layers", "encoder_attention_heads", "encoder_ffn_dim",
                  "num_mel_bins", "n_window", "n_window_infer", "conv_chunksize",

@@ -296,11 +296,16 @@ struct LayerOff {
 
 struct PackLayout {
   size_t conv1_w, conv1_b, conv2_w, conv2_b, conv3_w, conv3_b, conv_out_w, conv_out_b, pe;
+  size_t conv2_s, conv3_s, conv_out_s;  // AUT_FP8_CONV: MX scales of the conv-stem weights
   std::vector<LayerOff> layers;
   size_t ln_post_g, ln_post_b, proj1_w, proj1_b, proj2_w, proj2_b;
   size_t proj1_s, proj2_s;
   size_t total;
 };
+
+// channels per pixel of the MX-fp8 conv-stem activations: a multiple of 128,
+// so that a 128-code k step of the implicit convolution stays within one tap
+int conv_cp(const Geometry& g) { return (g.C + 127) / 128 * 128; }
 
 // the AUT_FP8_* bits in force for a dtype
 int fp8_mask(const aut_config& c, aut_dtype dt) { return dt == AUT_FP8 ? c.fp8_gemms : 0; }
@@ -327,11 +332,24 @@ PackLayout pack_layout(const Geometry& g, aut_dtype dt, int f8) {
   const size_t C = g.C, d = g.d, F = g.F, O = g.out;
   L.conv1_w = take(C * 9 * 4);
   L.conv1_b = take(C * 4);
-  L.conv2_w = take(C * 9 * C * es);
-  L.conv2_b = take(C * 4);
-  L.conv3_w = take(C * 9 * C * es);
-  L.conv3_b = take(C * 4);
-  L.conv_out_w = take(d * g.h3 * C * es);
+  L.conv2_s = L.conv3_s = L.conv_out_s = 0;
+  if (f8 & AUT_FP8_CONV) {
+    const size_t cp = conv_cp(g);
+    L.conv2_w = take(C * 9 * cp);
+    L.conv2_s = take(aut::mx_scale_bytes((long)C, (int)(9 * cp)));
+    L.conv2_b = take(C * 4);
+    L.conv3_w = take(C * 9 * cp);
+    L.conv3_s = take(aut::mx_scale_bytes((long)C, (int)(9 * cp)));
+    L.conv3_b = take(C * 4);
+    L.conv_out_w = take(d * g.h3 * cp);
+    L.conv_out_s = take(aut::mx_scale_bytes((long)d, (int)(g.h3 * cp)));
+  } else {
+    L.conv2_w = take(C * 9 * C * es);
+    L.conv2_b = take(C * 4);
+    L.conv3_w = take(C * 9 * C * es);
+    L.conv3_b = take(C * 4);
+    L.conv_out_w = take(d * g.h3 * C * es);
+  }
   L.conv_out_b = take(d * 4);
   L.pe = take((size_t)g.w3 * d * 4);
   L.layers.resize(g.layers);
@@ -368,6 +386,8 @@ aut_status check_dtype(const aut_config& c, aut_dtype dt) {
   if (!valid_dtype(dt)) return fail(AUT_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   if (dt == AUT_FP8 && (c.d_model % 128 || c.encoder_ffn_dim % 128))
     return fail(AUT_ERR_UNSUPPORTED, "AUT_FP8 needs d_model and encoder_ffn_dim multiples of 128");
+  if (dt == AUT_FP8 && (c.fp8_gemms & AUT_FP8_CONV) && c.downsample_hidden_size % 32)
+    return fail(AUT_ERR_UNSUPPORTED, "AUT_FP8_CONV needs downsample_hidden_size a multiple of 32");
   return AUT_OK;
 }
 
@@ -448,12 +468,23 @@ extern "C" aut_status aut_weights_pack(const aut_config* cfg, const aut_weight_p
   const int C = g.C, d = g.d, F = g.F;
   HIPCHK(aut::launch_pack(w->conv1_w, base + L.conv1_w, AUT_FP32, aut::PACK_CAST, C, 9, 0, 0, s));
   HIPCHK(vec(w->conv1_b, L.conv1_b, C));
-  HIPCHK(aut::launch_pack(w->conv2_w, base + L.conv2_w, bdt, aut::PACK_CONV, C, 9 * C, C, 0, s));
+  if (f8 & AUT_FP8_CONV) {
+    const int cp = conv_cp(g);
+    HIPCHK(aut::launch_mx_quantize_gather(w->conv2_w, aut::PACK_CONV, C, C, cp, 1,
+                                          (uint8_t*)(base + L.conv2_w), (uint8_t*)(base + L.conv2_s), s));
+    HIPCHK(aut::launch_mx_quantize_gather(w->conv3_w, aut::PACK_CONV, C, C, cp, 1,
+                                          (uint8_t*)(base + L.conv3_w), (uint8_t*)(base + L.conv3_s), s));
+    HIPCHK(aut::launch_mx_quantize_gather(w->conv_out_w, aut::PACK_CONV_OUT, d, C, cp, g.h3,
+                                          (uint8_t*)(base + L.conv_out_w),
+                                          (uint8_t*)(base + L.conv_out_s), s));
+  } else {
+    HIPCHK(aut::launch_pack(w->conv2_w, base + L.conv2_w, bdt, aut::PACK_CONV, C, 9 * C, C, 0, s));
+    HIPCHK(aut::launch_pack(w->conv3_w, base + L.conv3_w, bdt, aut::PACK_CONV, C, 9 * C, C, 0, s));
+    HIPCHK(aut::launch_pack(w->conv_out_w, base + L.conv_out_w, bdt, aut::PACK_CONV_OUT, d,
+                            g.h3 * C, C, g.h3, s));
+  }
   HIPCHK(vec(w->conv2_b, L.conv2_b, C));
-  HIPCHK(aut::launch_pack(w->conv3_w, base + L.conv3_w, bdt, aut::PACK_CONV, C, 9 * C, C, 0, s));
   HIPCHK(vec(w->conv3_b, L.conv3_b, C));
-  HIPCHK(aut::launch_pack(w->conv_out_w, base + L.conv_out_w, bdt, aut::PACK_CONV_OUT, d,
-                          g.h3 * C, C, g.h3, s));
   if (cfg->conv_out_bias) HIPCHK(vec(w->conv_out_b, L.conv_out_b, d));
   HIPCHK(aut::launch_pe_table((float*)(base + L.pe), g.w3, d, s));
   for (int i = 0; i < g.layers; ++i) {
@@ -489,6 +520,7 @@ namespace {
 struct WsLayout {
   size_t chunks, rowmap, cu, worder;
   size_t a1, a2, a3;
+  size_t a1_s, a2_s, a3_s;  // AUT_FP8_CONV: MX scales of the conv-stem activations
   size_t x, xn, qkv, o, h;
   size_t xn_s, o_s, h_s;  // AUT_FP8: MX scales of xn, o and h
   size_t total;
@@ -509,8 +541,11 @@ WsLayout ws_layout(const aut_plan_t& p, aut_dtype dt) {
   const size_t nch = p.chunks.size();
   const size_t nw = p.cu.size() - 1;
   // chunks per conv-stem batch: conv_chunksize, also kept small enough that
-  // the batch's conv1 output stays below 2 GiB (32-bit buffer offsets)
-  const size_t per_chunk = (size_t)g.h1 * g.w1 * g.C * es;
+  // the batch's conv1 output stays below 2 GiB (32-bit buffer offsets); an
+  // MX-fp8 stem stores cp one-byte codes per pixel
+  const bool f8c = dt == AUT_FP8 && (p.cfg.fp8_gemms & AUT_FP8_CONV);
+  const size_t cs = f8c ? std::max<size_t>(g.C * es, (size_t)conv_cp(g)) : g.C * es;
+  const size_t per_chunk = (size_t)g.h1 * g.w1 * cs;
   const size_t max_nb = std::max<size_t>(1, ((size_t)1 << 31) / per_chunk - 1);
   W.nb = (int)std::min<size_t>(std::min<size_t>((size_t)p.cfg.conv_chunksize, nch), max_nb);
   const size_t nb = (size_t)W.nb;
@@ -518,9 +553,16 @@ WsLayout ws_layout(const aut_plan_t& p, aut_dtype dt) {
   W.rowmap = take(T * 4);
   W.cu = take((nw + 1) * 4);
   W.worder = take(nw * 4);
-  W.a1 = take(nb * g.h1 * g.w1 * g.C * es);
-  W.a2 = take(nb * g.h2 * g.w2 * g.C * es);
-  W.a3 = take(nb * g.h3 * g.w3 * g.C * es);
+  W.a1 = take(nb * g.h1 * g.w1 * cs);
+  W.a2 = take(nb * g.h2 * g.w2 * cs);
+  W.a3 = take(nb * g.h3 * g.w3 * cs);
+  W.a1_s = W.a2_s = W.a3_s = 0;
+  if (f8c) {
+    const size_t spp = (size_t)conv_cp(g) / 32;  // scale bytes per pixel
+    W.a1_s = take(nb * g.h1 * g.w1 * spp);
+    W.a2_s = take(nb * g.h2 * g.w2 * spp);
+    W.a3_s = take(nb * g.h3 * g.w3 * spp);
+  }
   W.x = take(T * g.d * 4);
   W.xn = take(T * g.d * es);
   W.qkv = take(T * 3 * g.d * es);
@@ -658,11 +700,12 @@ aut_status gemm(const Ctx& c, aut_kernel_class cls, const aut::GemmArgs& a, int 
   return AUT_OK;
 }
 
-aut_status gemm_f8(const Ctx& c, const aut::GemmArgs& a, int epi, double bytes) {
+aut_status gemm_f8(const Ctx& c, aut_kernel_class cls, const aut::GemmArgs& a, int amode, int epi,
+                   double bytes) {
   aut::prof_begin(c.s);
-  hipError_t e = aut::launch_gemm_f8(a, epi, c.s);
+  hipError_t e = aut::launch_gemm_f8(a, amode, epi, c.s);
   if (e != hipSuccess) return fail(AUT_ERR_HIP, "fp8 gemm launch failed: %s", hipGetErrorString(e));
-  aut::prof_end(c.s, AUT_K_GEMM_FP8, 2.0 * a.M * (double)a.N * a.K, bytes);
+  aut::prof_end(c.s, cls, 2.0 * a.M * (double)a.N * a.K, bytes);
   return AUT_OK;
 }
 
@@ -676,13 +719,18 @@ aut::GemmArgs plain_args(const void* A, const void* B, int M, int N, int K, cons
   return a;
 }
 
-// frontend: features -> hidden [T, d] fp32
+// frontend: features -> hidden [T, d] fp32.  Under AUT_FP8_CONV the stem's
+// activations are MX-fp8 codes, cp channels per pixel (zero past C), with
+// row-major scales per pixel, and conv2, conv3 and conv_out run on them.
 aut_status run_frontend(const Ctx& c, const float* feat, int T_max, float* hidden) {
   const aut_plan_t& p = *c.p;
   const Geometry& g = *c.g;
   const WsLayout& W = *c.W;
   const PackLayout& P = *c.P;
   const size_t es = esize(c.dt);
+  const bool f8 = c.f8 & AUT_FP8_CONV;
+  const int cp = conv_cp(g);
+  const size_t cs = f8 ? (size_t)cp : (size_t)g.C * es;  // bytes per pixel of the stem activations
   const int nch = (int)p.chunks.size();
   const int* d_chunks = (const int*)(c.ws + W.chunks);
   const int* d_rowmap = (const int*)(c.ws + W.rowmap);
@@ -691,10 +739,11 @@ aut_status run_frontend(const Ctx& c, const float* feat, int T_max, float* hidde
     // conv1 + GELU
     aut::prof_begin(c.s);
     hipError_t e = aut::launch_conv1(feat, T_max, d_chunks, c0, n, pk_at<float>(c, P.conv1_w),
-                                     pk_at<float>(c, P.conv1_b), c.ws + W.a1, c.dt, g, c.s);
+                                     pk_at<float>(c, P.conv1_b), c.ws + W.a1, f8 ? AUT_FP8 : c.dt,
+                                     g, c.s, f8 ? (uint8_t*)(c.ws + W.a1_s) : nullptr, cp);
     if (e != hipSuccess) return fail(AUT_ERR_HIP, "conv1 launch failed: %s", hipGetErrorString(e));
     aut::prof_end(c.s, AUT_K_CONV1, 2.0 * 9 * g.C * (double)g.h1 * g.w1 * n,
-                  (double)n * g.mel * g.cf * 4 + (double)n * g.h1 * g.w1 * g.C * es);
+                  (double)n * g.mel * g.cf * 4 + (double)n * g.h1 * g.w1 * cs);
     // conv2, conv3: implicit GEMMs over the whole (padded) chunks
     for (int layer = 2; layer <= 3; ++layer) {
       aut::GemmArgs a;
@@ -702,23 +751,42 @@ aut_status run_frontend(const Ctx& c, const float* feat, int T_max, float* hidde
       const bool l2 = layer == 2;
       a.A = c.ws + (l2 ? W.a1 : W.a2);
       a.B = c.pk + (l2 ? P.conv2_w : P.conv3_w);
-      a.ldb = 9 * g.C;
       a.hin = l2 ? g.h1 : g.h2;
       a.win = l2 ? g.w1 : g.w2;
       a.hout = l2 ? g.h2 : g.h3;
       a.wout = l2 ? g.w2 : g.w3;
-      a.cin = g.C;
       a.xmajor = l2 ? 0 : 1;  // conv3 output stored [chunk][x][y][c] for the token flatten
       a.M = n * a.hout * a.wout;
       a.N = g.C;
-      a.K = 9 * g.C;
-      a.a_bytes = (size_t)n * a.hin * a.win * g.C * es;
       a.bias = pk_at<float>(c, l2 ? P.conv2_b : P.conv3_b);
       a.out = c.ws + (l2 ? W.a2 : W.a3);
-      a.ldo = g.C;
-      const double bytes = ((double)n * a.hin * a.win * g.C + (double)g.C * a.K +
-                            (double)a.M * g.C) * es;
-      aut_status st = gemm(c, AUT_K_CONV_GEMM, a, aut::A_CONV, aut::EPI_STORE_GELU, bytes);
+      aut_status st;
+      if (f8) {
+        a.cin = cp;
+        a.K = 9 * cp;
+        a.ldb = 9 * cp;
+        a.a_bytes = (size_t)n * a.hin * a.win * cp;
+        a.a_scale = (const uint8_t*)(c.ws + (l2 ? W.a1_s : W.a2_s));
+        a.a_scale_ld = cp / 32;
+        a.a_scale_bytes = (size_t)n * a.hin * a.win * (cp / 32);
+        a.b_scale = (const uint8_t*)(c.pk + (l2 ? P.conv2_s : P.conv3_s));
+        a.ldo = cp;
+        a.n_store = cp;
+        a.out_scale = (uint8_t*)(c.ws + (l2 ? W.a2_s : W.a3_s));
+        a.out_scale_rowmajor = 1;
+        const double bytes = ((double)n * a.hin * a.win + (double)a.M) * cp * (1.0 + 1.0 / 32) +
+                             (double)g.C * a.K * (1.0 + 1.0 / 32);
+        st = gemm_f8(c, AUT_K_CONV_GEMM, a, aut::A_CONV, aut::EPI_GELU_MX, bytes);
+      } else {
+        a.cin = g.C;
+        a.K = 9 * g.C;
+        a.ldb = 9 * g.C;
+        a.a_bytes = (size_t)n * a.hin * a.win * g.C * es;
+        a.ldo = g.C;
+        const double bytes = ((double)n * a.hin * a.win * g.C + (double)g.C * a.K +
+                              (double)a.M * g.C) * es;
+        st = gemm(c, AUT_K_CONV_GEMM, a, aut::A_CONV, aut::EPI_STORE_GELU, bytes);
+      }
       if (st != AUT_OK) return st;
     }
     // conv_out + positions over the batch's valid tokens
@@ -728,22 +796,37 @@ aut_status run_frontend(const Ctx& c, const float* feat, int T_max, float* hidde
       aut::GemmArgs a;
       memset(&a, 0, sizeof(a));
       a.A = c.ws + W.a3;
-      a.lda = (long)g.h3 * g.C;
       a.B = c.pk + P.conv_out_w;
-      a.ldb = (long)g.h3 * g.C;
       a.M = r1 - r0;
       a.N = g.d;
-      a.K = g.h3 * g.C;
       a.rowmap = d_rowmap + r0;
       a.rowmap_base = c0 * g.w3;
-      a.a_bytes = (size_t)n * g.w3 * g.h3 * g.C * es;
       a.tpc = g.w3;
       a.bias = p.cfg.conv_out_bias ? pk_at<float>(c, P.conv_out_b) : nullptr;
       a.out = hidden + (size_t)r0 * g.d;
       a.ldo = g.d;
       a.pe = pk_at<float>(c, P.pe);
-      const double bytes = ((double)a.M * a.K + (double)g.d * a.K) * es + (double)a.M * g.d * 4;
-      aut_status st = gemm(c, AUT_K_CONV_OUT, a, aut::A_ROWMAP, aut::EPI_PE, bytes);
+      aut_status st;
+      if (f8) {
+        a.lda = (long)g.h3 * cp;
+        a.ldb = (long)g.h3 * cp;
+        a.K = g.h3 * cp;
+        a.a_bytes = (size_t)n * g.w3 * g.h3 * cp;
+        a.a_scale = (const uint8_t*)(c.ws + W.a3_s);
+        a.a_scale_ld = g.h3 * cp / 32;
+        a.a_scale_bytes = (size_t)n * g.w3 * g.h3 * (cp / 32);
+        a.b_scale = (const uint8_t*)(c.pk + P.conv_out_s);
+        const double bytes = ((double)a.M * a.K + (double)g.d * a.K) * (1.0 + 1.0 / 32) +
+                             (double)a.M * g.d * 4;
+        st = gemm_f8(c, AUT_K_CONV_OUT, a, aut::A_ROWMAP, aut::EPI_PE, bytes);
+      } else {
+        a.lda = (long)g.h3 * g.C;
+        a.ldb = (long)g.h3 * g.C;
+        a.K = g.h3 * g.C;
+        a.a_bytes = (size_t)n * g.w3 * g.h3 * g.C * es;
+        const double bytes = ((double)a.M * a.K + (double)g.d * a.K) * es + (double)a.M * g.d * 4;
+        st = gemm(c, AUT_K_CONV_OUT, a, aut::A_ROWMAP, aut::EPI_PE, bytes);
+      }
       if (st != AUT_OK) return st;
     }
   }
@@ -797,7 +880,7 @@ aut_status run_encode(const Ctx& c, float* out) {
     if (!f8) return gemm(c, AUT_K_GEMM, a, aut::A_PLAIN, epi, bytes_base);
     a.a_scale = a_s;
     a.b_scale = (const uint8_t*)(c.pk + b_s);
-    return gemm_f8(c, a, epi, bytes_f8);
+    return gemm_f8(c, AUT_K_GEMM_FP8, a, aut::A_PLAIN, epi, bytes_f8);
   };
   aut_status st;
   for (int i = 0; i < g.layers; ++i) {
@@ -1152,7 +1235,7 @@ extern "C" aut_status aut_mx_matmul(const uint8_t* a_codes, const uint8_t* a_sca
   a.M = (int)M; a.N = N; a.K = K;
   a.out = out; a.ldo = N;
   a.a_scale = a_scales; a.b_scale = b_scales;
-  hipError_t e = aut::launch_gemm_f8(a, aut::EPI_STORE_F32, (hipStream_t)stream);
+  hipError_t e = aut::launch_gemm_f8(a, aut::A_PLAIN, aut::EPI_STORE_F32, (hipStream_t)stream);
   if (e != hipSuccess) return fail(AUT_ERR_HIP, "mx matmul launch failed: %s", hipGetErrorString(e));
   return AUT_OK;
 }

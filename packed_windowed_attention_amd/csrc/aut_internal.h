@@ -53,9 +53,12 @@ hipError_t launch_pack(const float* src, void* dst, aut_dtype dt, int mode, int 
 hipError_t launch_pe_table(float* pe, int rows, int d, hipStream_t s);
 
 // conv1 + GELU over `nb` chunks starting at chunk_first of the plan.
+// AUT_FP8: MX-fp8 codes [pixel][cp] (channels past C zero) into a1 and their
+// scales, row-major cp / 32 bytes per pixel, into a1_scales.
 hipError_t launch_conv1(const float* feat, int T_max, const int* chunks, int chunk_first, int nb,
                         const float* w1, const float* b1, void* a1, aut_dtype dt,
-                        const Geometry& g, hipStream_t s);
+                        const Geometry& g, hipStream_t s, uint8_t* a1_scales = nullptr,
+                        int cp = 0);
 
 // Generic MFMA GEMM: C[M, N] = A[M, K] * B[N, K]^T with an A-gather mode and
 // an epilogue.
@@ -86,6 +89,15 @@ struct GemmArgs {
   const uint8_t* a_scale;
   const uint8_t* b_scale;
   uint8_t* out_scale;
+  // A_CONV / A_ROWMAP under fp8: A's scales are row-major, a_scale_ld bytes
+  // per row (per input pixel for A_CONV, per gathered row for A_ROWMAP)
+  int a_scale_ld;
+  size_t a_scale_bytes;  // bytes of A's scale array (gathered modes)
+  // EPI_GELU_MX: columns written (>= N; the ones past N as zero codes), and
+  // the output's scale layout: 0 = mx_scale_index over n_store columns,
+  // 1 = row-major, n_store / 32 bytes per row
+  int n_store;
+  int out_scale_rowmajor;
 };
 // bf16 runs the 256-row kernel (k_gemm256.hip), fp32 the 128 x 128 one
 // (k_gemm128.hip).
@@ -94,9 +106,18 @@ hipError_t launch_gemm128(const GemmArgs& a, int amode, int epi, aut_dtype dt, h
 hipError_t launch_gemm256(const GemmArgs& a, int amode, int epi, hipStream_t s);
 
 // MX-fp8 products: A [M, K] and B [N, K] as e4m3 codes (lda, ldb in bytes)
-// with scales; K a multiple of 128.  Epilogues EPI_STORE, EPI_STORE_GELU,
-// EPI_RESID, EPI_STORE_F32, EPI_GELU_MX.
-hipError_t launch_gemm_f8(const GemmArgs& a, int epi, hipStream_t s);
+// with scales; K a multiple of 128.  A modes: A_PLAIN (scales in the
+// mx_scale_index layout), A_CONV (cin a multiple of 128, so a k step stays in
+// one tap) and A_ROWMAP (row-major scales).  Epilogues: A_PLAIN with
+// EPI_STORE, EPI_STORE_GELU, EPI_RESID, EPI_STORE_F32, EPI_GELU_MX; A_CONV
+// with EPI_GELU_MX; A_ROWMAP with EPI_PE.
+hipError_t launch_gemm_f8(const GemmArgs& a, int amode, int epi, hipStream_t s);
+
+// conv-stem weights straight from their PyTorch layout to MX-fp8, channels
+// padded to cp with zeros: mode PACK_CONV, [Co, Ci, 3, 3] -> [Co][tap * cp + c];
+// PACK_CONV_OUT, [d, C * F] (c * F + f) -> [d][f * cp + c].
+hipError_t launch_mx_quantize_gather(const float* src, int mode, int rows, int C, int cp, int F,
+                                     uint8_t* codes, uint8_t* scales, hipStream_t s);
 
 // fp32 rows [R, K] (row stride ldx) -> MX-fp8 codes [R, K] and scales
 // (mx_scale_bytes(R, K) bytes, rows padded to 16 with scale code 0).

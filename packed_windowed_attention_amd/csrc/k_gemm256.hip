@@ -158,6 +158,7 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& p, int m0, int n
       // a thread per 32-value block of a staged row: its maximum, the scale
       // exponent, 32 codes in two 16-byte stores and the scale byte
       constexpr int BPR = BN / MX_BLOCK;
+      const int ncols = p.n_store > N ? p.n_store : N;   // columns past N: zero codes
 #pragma unroll
       for (int q = tid; q < PR * BPR; q += NT) {
         const int r = q / BPR;
@@ -175,7 +176,7 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& p, int m0, int n
           f[k] = __builtin_bit_cast(f32x4_t, src[k]);
           amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f[k][0]), fabsf(f[k][1])), fmaxf(fabsf(f[k][2]), fabsf(f[k][3]))));
         }
-        if (m < M && n < N) {
+        if (m < M && n < ncols) {
           const int e = mx_exponent(amax);
           unsigned int w[8];
 #pragma unroll
@@ -185,7 +186,8 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& p, int m0, int n
           u32x4_t* dst = reinterpret_cast<u32x4_t*>((uint8_t*)p.out + (size_t)m * p.ldo + n);
           dst[0] = u32x4_t{w[0], w[1], w[2], w[3]};
           dst[1] = u32x4_t{w[4], w[5], w[6], w[7]};
-          p.out_scale[mx_scale_index(m, n / MX_BLOCK, N)] = (uint8_t)(e + 127);
+          p.out_scale[p.out_scale_rowmajor ? (size_t)m * (ncols / MX_BLOCK) + n / MX_BLOCK
+                                           : mx_scale_index(m, n / MX_BLOCK, ncols)] = (uint8_t)(e + 127);
         }
       }
       continue;
@@ -641,7 +643,13 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
 // 16-row group (mx_scale_index); they travel with the step's tiles, straight
 // into LDS (one 256-byte load per four groups), and each lane reads its byte
 // there: no scale registers live across steps.
-template <int BN, int EPI>
+//
+// A-gather modes as in the bf16 kernels, on codes (one byte per element): the
+// implicit 3x3 stride-2 convolution needs cin a multiple of 128 so that a k
+// step stays within one tap.  Their scales are row-major (a_scale_ld bytes per
+// input pixel or gathered row); a step's four blocks of a row are then four
+// consecutive bytes, one 4-byte load per row into an LDS table [row][4].
+template <int BN, int AMODE, int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   constexpr int NT8 = 512;
@@ -652,13 +660,13 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   constexpr int A_LOADS = A_UNITS / NT8;
   constexpr int B_LOADS = B_UNITS / NT8;
   constexpr int BK8 = 128;                   // codes per row per k step
-  constexpr int SA_Q = BM / 64;              // 256-byte scale loads per step: 4 groups each
+  constexpr int SA_Q = BM / 64;              // 256-byte scale loads per step: 4 groups / 64 rows each
   constexpr int SB_Q = BN / 64;
   static_assert(B_UNITS % NT8 == 0 && BN % 64 == 0, "whole loads per thread");
   static_assert(SA_Q + SB_Q <= 16, "scale loads: at most two per wave");
   __shared__ u32x4_t As0[A_UNITS], As1[A_UNITS];
   __shared__ u32x4_t Bs0[B_UNITS], Bs1[B_UNITS];
-  __shared__ unsigned Sa0[BM], Sa1[BM], Sb0[BN], Sb1[BN];  // 64 bytes per 16 rows: 4 per row
+  __shared__ unsigned Sa0[BM], Sa1[BM], Sb0[BN], Sb1[BN];  // 4 scale bytes per row
 
   const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (tile >= nM * nN) return;
@@ -679,46 +687,144 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
 
   const int lrow8 = lane >> 3;
   const int lunit = (lane & 7) ^ lrow8;
-  const char* a_base = (const char*)p.A + (size_t)m0 * p.lda;
-  const unsigned a_bytes = (unsigned)((size_t)(M - m0) * p.lda);
+  const char* a_base;
+  unsigned a_bytes;
+  if (AMODE == A_PLAIN) {
+    a_base = (const char*)p.A + (size_t)m0 * p.lda;
+    a_bytes = (unsigned)((size_t)(M - m0) * p.lda);
+  } else {
+    a_base = (const char*)p.A;
+    a_bytes = (unsigned)p.a_bytes;
+  }
   const unsigned a_step = (unsigned)(64 * p.lda);
   const unsigned a_off0 = (unsigned)((wave * 8 + lrow8) * p.lda);
-  const char* b_base = (const char*)p.B + (size_t)n0 * p.ldb;
-  const unsigned b_bytes = (unsigned)((size_t)(N - n0) * p.ldb);
+  // A_ROWMAP: per-load row offsets; A_CONV: per-load chunk offset and pixel
+  unsigned a_rowoff[AMODE == A_PLAIN ? 1 : A_LOADS];
+  int a_pix[AMODE == A_CONV ? A_LOADS : 1];  // (oy << 16) | ox, or -1 past M
+  // output pixel of GEMM row m: {chunk, (oy << 16) | ox}
+  auto conv_pixel = [&](int m) __attribute__((always_inline)) {
+    const int hw = p.hout * p.wout;
+    const int chunk = m / hw;
+    const int rem = m - chunk * hw;
+    int oy, ox;
+    if (p.xmajor) {
+      ox = rem / p.hout;
+      oy = rem - ox * p.hout;
+    } else {
+      oy = rem / p.wout;
+      ox = rem - oy * p.wout;
+    }
+    return int2{chunk, (oy << 16) | ox};
+  };
+  if (AMODE != A_PLAIN) {
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j) {
+      const int m = m0 + (j * 8 + wave) * 8 + lrow8;
+      if (AMODE == A_ROWMAP) {
+        a_rowoff[j] = m < M ? (unsigned)((size_t)(p.rowmap[m] - p.rowmap_base) * p.lda) : OOB;
+      } else {
+        a_rowoff[j] = 0;
+        a_pix[j] = -1;
+        if (m < M) {
+          const int2 cpx = conv_pixel(m);
+          a_pix[j] = cpx.y;
+          a_rowoff[j] = (unsigned)((size_t)cpx.x * p.hin * p.win * p.cin);
+        }
+      }
+    }
+  }
+  // (an MX epilogue that writes zero columns past N may run tiles with n0 >= N:
+  // their B rows all load zero)
+  const char* b_base = (const char*)p.B + (size_t)(n0 < N ? n0 : 0) * p.ldb;
+  const unsigned b_bytes = n0 < N ? (unsigned)((size_t)(N - n0) * p.ldb) : 0u;
   const unsigned b_step = (unsigned)(64 * p.ldb);
   const unsigned b_off0 = (unsigned)((wave * 8 + lrow8) * p.ldb);
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t b_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_bytes, 0x00020000);
-  // Scale loads: wave w < SA_Q takes A groups 4 w .. 4 w + 3 of the tile,
-  // waves SA_Q .. SA_Q + SB_Q - 1 (mod 8) the B groups; lane l fills bytes
-  // 4 (l % 16) .. + 3 of group l / 16 of its four.  Groups past the operand's
-  // padded rows load zero.
-  const __amdgpu_buffer_rsrc_t sa_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)p.a_scale, (short)0, (int)(((M + 15) >> 4) * KS * 64), 0x00020000);
+  // Scale loads.  A_PLAIN: wave w < SA_Q takes A groups 4 w .. 4 w + 3 of the
+  // tile, lane l bytes 4 (l % 16) .. + 3 of group l / 16.  A_CONV / A_ROWMAP:
+  // wave w < SA_Q takes rows 64 w .. 64 w + 63, lane l row 64 w + l.  Waves
+  // SA_Q .. SA_Q + SB_Q - 1 (mod 8) take the B groups.  Loads past the scale
+  // array read zero.
+  const unsigned sa_bytes = AMODE == A_PLAIN ? (unsigned)(((M + 15) >> 4) * KS * 64)
+                                             : (unsigned)p.a_scale_bytes;
+  const __amdgpu_buffer_rsrc_t sa_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.a_scale, (short)0, (int)sa_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t sb_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.b_scale, (short)0, (int)(((N + 15) >> 4) * KS * 64), 0x00020000);
   const int sq_a = wave;                          // A quad of this wave, if < SA_Q
   const int sq_b0 = (wave - SA_Q) & 7;            // first B quad of this wave
   const int sgrp = lane >> 4, sbyte = 4 * (lane & 15);
+  // gathered modes: the scale row of this lane's load
+  unsigned s_rowoff = OOB;                        // A_ROWMAP: row * a_scale_ld
+  int s_pix = -1, s_chunkpix = 0;                 // A_CONV: (oy << 16) | ox, chunk * hin * win
+  if (AMODE != A_PLAIN && sq_a < SA_Q) {
+    const int m = m0 + 64 * sq_a + lane;
+    if (m < M) {
+      if (AMODE == A_ROWMAP) {
+        s_rowoff = (unsigned)((size_t)(p.rowmap[m] - p.rowmap_base) * p.a_scale_ld);
+      } else {
+        const int2 cpx = conv_pixel(m);
+        s_pix = cpx.y;
+        s_chunkpix = cpx.x * p.hin * p.win;
+      }
+    }
+  }
 
   auto issue = [&](int kt, u32x4_t* As_s, u32x4_t* Bs_s, unsigned* Sa_s, unsigned* Sb_s)
       __attribute__((always_inline)) {
-    const unsigned koff = (unsigned)(kt * BK8 + lunit * 16);
+    if (AMODE == A_CONV) {
+      const int k = kt * BK8 + lunit * 16;
+      const int tap = k / p.cin;
+      const int ci = k - tap * p.cin;
+      const int kh = tap / 3;
+      const int kw = tap - 3 * kh;
 #pragma unroll
-    for (int j = 0; j < A_LOADS; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(j * 8 + wave) * 64]), 16,
-                                               a_off0 + j * a_step + koff, 0, 0, 0);
+      for (int j = 0; j < A_LOADS; ++j) {
+        const int oy = a_pix[j] >> 16, ox = a_pix[j] & 0xFFFF;
+        const int iy = 2 * oy + kh - 1;
+        const int ix = 2 * ox + kw - 1;
+        const bool ok = a_pix[j] >= 0 && iy >= 0 && iy < p.hin && ix >= 0 && ix < p.win;
+        const unsigned off = ok ? a_rowoff[j] + (unsigned)((iy * p.win + ix) * p.cin + ci) : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(j * 8 + wave) * 64]), 16,
+                                                 off, 0, 0, 0);
+      }
+    } else {
+      const unsigned koff = (unsigned)(kt * BK8 + lunit * 16);
+#pragma unroll
+      for (int j = 0; j < A_LOADS; ++j) {
+        const unsigned off = AMODE == A_PLAIN ? a_off0 + j * a_step + koff
+                                              : (a_rowoff[j] == OOB ? OOB : a_rowoff[j] + koff);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(j * 8 + wave) * 64]), 16,
+                                                 off, 0, 0, 0);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < B_LOADS; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dma_dst(&Bs_s[(j * 8 + wave) * 64]), 16,
-                                               b_off0 + j * b_step + koff, 0, 0, 0);
+                                               b_off0 + j * b_step + (unsigned)(kt * BK8 + lunit * 16),
+                                               0, 0, 0);
     if (sq_a < SA_Q) {
-      const int grp = (m0 >> 4) + 4 * sq_a + sgrp;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          sa_rsrc, dma_dst((const u32x4_t*)&Sa_s[64 * sq_a]), 4,
-          (unsigned)((grp * KS + kt) * 64 + sbyte), 0, 0, 0);
+      unsigned off;
+      if (AMODE == A_PLAIN) {
+        const int grp = (m0 >> 4) + 4 * sq_a + sgrp;
+        off = (unsigned)((grp * KS + kt) * 64 + sbyte);
+      } else if (AMODE == A_ROWMAP) {
+        off = s_rowoff == OOB ? OOB : s_rowoff + 4 * kt;
+      } else {
+        const int tap = (kt * BK8) / p.cin;
+        const int cb = ((kt * BK8) - tap * p.cin) / MX_BLOCK;
+        const int kh = tap / 3;
+        const int kw = tap - 3 * kh;
+        const int iy = 2 * (s_pix >> 16) + kh - 1;
+        const int ix = 2 * (s_pix & 0xFFFF) + kw - 1;
+        const bool ok = s_pix >= 0 && iy >= 0 && iy < p.hin && ix >= 0 && ix < p.win;
+        off = ok ? (unsigned)((s_chunkpix + iy * p.win + ix) * p.a_scale_ld + cb) : OOB;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sa_rsrc, dma_dst((const u32x4_t*)&Sa_s[64 * sq_a]), 4,
+                                               off, 0, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -748,7 +854,9 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (kt + 1 < KS) issue(kt + 1, As_n, Bs_n, Sa_n, Sb_n);
-    const uint8_t* sa = (const uint8_t*)Sa_s + wm * 512 + lane;   // group wm * 8 + i: byte 64 i
+    // A_PLAIN: group wm * 8 + i, byte 64 i + lane; gathered: row wm * 128 + 16 i + lrow, byte g
+    const uint8_t* sa = AMODE == A_PLAIN ? (const uint8_t*)Sa_s + wm * 512 + lane
+                                         : (const uint8_t*)Sa_s + (wm * 128 + lrow) * 4 + g;
     const uint8_t* sb = (const uint8_t*)Sb_s + wn * (WN * 4) + lane;
     i32x8_t wb[NTW];
     int sw[NTW];
@@ -762,7 +870,7 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
     for (int i = 0; i < 8; ++i) {
       const int r = wm * 128 + 16 * i + lrow;
       const i32x8_t xa = units_to_i32x8(As_s[r * KU + swz(g, r)], As_s[r * KU + swz(g + 4, r)]);
-      const int sx = sa[64 * i];
+      const int sx = sa[64 * i];   // 64 bytes per 16 rows in both layouts
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
         acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb[j], xa, acc[j][i], 0, 0, 0,
@@ -779,14 +887,16 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   staged_epilogue<BN, WN, NT8, EPI>(p, m0, n0, wm, wn, tid, acc, As0, As1, Bs0, Bs1);
 }
 
-template <int BN, int EPI>
+template <int BN, int AMODE, int EPI>
 hipError_t run8_f8(const GemmArgs& a, hipStream_t s) {
   const int nM = (a.M + BM - 1) / BM;
-  const int nN = (a.N + BN - 1) / BN;
+  // an MX epilogue also writes the zero columns up to n_store
+  const int ncols = EPI == EPI_GELU_MX && a.n_store > a.N ? a.n_store : a.N;
+  const int nN = (ncols + BN - 1) / BN;
   const int tiles = nM * nN;
   const int per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL((gemm8w_f8_kernel<BN, EPI>), dim3(8 * per_xcd), dim3(512), 0, s, a, nM, nN,
-                     per_xcd);
+  hipLaunchKernelGGL((gemm8w_f8_kernel<BN, AMODE, EPI>), dim3(8 * per_xcd), dim3(512), 0, s, a, nM,
+                     nN, per_xcd);
   return hipGetLastError();
 }
 
@@ -867,7 +977,10 @@ int pick_bn(int M, int N) {
 // output rows
 bool epilogue_fits(const GemmArgs& a, int epi) {
   if ((size_t)a.out & 15) return false;
-  if (epi == EPI_GELU_MX) return a.N % 128 == 0 && a.ldo % 16 == 0 && a.out_scale != nullptr;
+  if (epi == EPI_GELU_MX) {
+    const int ncols = a.n_store > a.N ? a.n_store : a.N;
+    return ncols % 128 == 0 && a.ldo % 16 == 0 && a.ldo >= ncols && a.out_scale != nullptr;
+  }
   const int epc = (epi == EPI_STORE || epi == EPI_STORE_GELU) ? 8 : 4;
   return a.N % epc == 0 && a.ldo % epc == 0;
 }
@@ -879,15 +992,22 @@ int g_gemm256_force_bn = 0;  // tuning hook: 0 = automatic
 namespace {
 
 template <int BN>
-hipError_t dispatch_f8(const GemmArgs& a, int epi, hipStream_t s) {
-  switch (epi) {
-    case EPI_STORE: return run8_f8<BN, EPI_STORE>(a, s);
-    case EPI_STORE_GELU: return run8_f8<BN, EPI_STORE_GELU>(a, s);
-    case EPI_RESID: return run8_f8<BN, EPI_RESID>(a, s);
-    case EPI_STORE_F32: return run8_f8<BN, EPI_STORE_F32>(a, s);
-    case EPI_GELU_MX: return run8_f8<BN, EPI_GELU_MX>(a, s);
-    default: return hipErrorInvalidValue;
+hipError_t dispatch_f8(const GemmArgs& a, int amode, int epi, hipStream_t s) {
+  if (amode == A_PLAIN) {
+    switch (epi) {
+      case EPI_STORE: return run8_f8<BN, A_PLAIN, EPI_STORE>(a, s);
+      case EPI_STORE_GELU: return run8_f8<BN, A_PLAIN, EPI_STORE_GELU>(a, s);
+      case EPI_RESID: return run8_f8<BN, A_PLAIN, EPI_RESID>(a, s);
+      case EPI_STORE_F32: return run8_f8<BN, A_PLAIN, EPI_STORE_F32>(a, s);
+      case EPI_GELU_MX: return run8_f8<BN, A_PLAIN, EPI_GELU_MX>(a, s);
+      default: break;
+    }
+  } else if (amode == A_CONV && epi == EPI_GELU_MX) {
+    return run8_f8<BN, A_CONV, EPI_GELU_MX>(a, s);
+  } else if (amode == A_ROWMAP && epi == EPI_PE) {
+    return run8_f8<BN, A_ROWMAP, EPI_PE>(a, s);
   }
+  return hipErrorInvalidValue;
 }
 
 // column tile of the fp8 kernel: 320 or 256, whichever fills the 256 CUs'
@@ -913,14 +1033,19 @@ int pick_bn_f8(int M, int N) {
 
 int g_gemm_f8_force_bn = 0;  // tuning hook: 0 = automatic
 
-hipError_t launch_gemm_f8(const GemmArgs& a, int epi, hipStream_t s) {
+hipError_t launch_gemm_f8(const GemmArgs& a, int amode, int epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K <= 0 || a.K % 128 || a.lda % 16 || a.ldb % 16 || !a.a_scale || !a.b_scale ||
       ((size_t)a.A & 15) || ((size_t)a.B & 15) || !epilogue_fits(a, epi))
     return hipErrorInvalidValue;
+  // gathered A: a k step within one tap, whole 4-byte scale rows, 32-bit offsets
+  if (amode == A_CONV && (a.cin % 128 || a.K != 9 * a.cin)) return hipErrorInvalidValue;
+  if (amode != A_PLAIN && (a.a_scale_ld % 4 || a.a_scale_bytes >= ((size_t)1 << 31) ||
+                           a.a_bytes >= ((size_t)1 << 31)))
+    return hipErrorInvalidValue;
   const int bn = g_gemm_f8_force_bn ? g_gemm_f8_force_bn : pick_bn_f8(a.M, a.N);
-  if (bn == 320) return dispatch_f8<320>(a, epi, s);
-  if (bn == 256) return dispatch_f8<256>(a, epi, s);
+  if (bn == 320) return dispatch_f8<320>(a, amode, epi, s);
+  if (bn == 256) return dispatch_f8<256>(a, amode, epi, s);
   return hipErrorInvalidValue;
 }
 

@@ -48,7 +48,63 @@ __global__ __launch_bounds__(MXQ_THREADS) void mx_quantize_kernel(const float* _
   scales[mx_scale_index(r, kb, K)] = (uint8_t)(e + 127);
 }
 
+// The same per block, reading a conv-stem weight from its PyTorch layout
+// (PACK_CONV / PACK_CONV_OUT, channels padded to cp with zeros).
+__global__ __launch_bounds__(MXQ_THREADS) void mx_quantize_gather_kernel(
+    const float* __restrict__ src, int mode, int R, int C, int cp, int F,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int per = mode == PACK_CONV ? 9 : F;     // taps or frequency bins
+  const int K = per * cp;
+  const int nkb = K / MX_BLOCK;
+  const long R16 = ((long)R + 15) / 16 * 16;
+  const long idx = (long)blockIdx.x * MXQ_THREADS + threadIdx.x;
+  if (idx >= R16 * nkb) return;
+  const int r = (int)(idx / nkb);
+  const int kb = (int)(idx - (long)r * nkb);
+  if (r >= R) {
+    scales[mx_scale_index(r, kb, K)] = 0;
+    return;
+  }
+  const int outer = (kb * MX_BLOCK) / cp;        // tap or bin (cp is a multiple of 32)
+  const int c0 = kb * MX_BLOCK - outer * cp;
+  float v[MX_BLOCK];
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < MX_BLOCK; ++j) {
+    const int c = c0 + j;
+    float x = 0.f;
+    if (c < C)
+      x = mode == PACK_CONV ? src[((size_t)r * C + c) * 9 + outer]
+                            : src[(size_t)r * C * F + (size_t)c * F + outer];
+    v[j] = x;
+    amax = fmaxf(amax, fabsf(x));
+  }
+  const int e = mx_exponent(amax);
+  unsigned int w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    w[i] = pack_fp8x4(mx_scale_down(v[4 * i], e), mx_scale_down(v[4 * i + 1], e),
+                      mx_scale_down(v[4 * i + 2], e), mx_scale_down(v[4 * i + 3], e));
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(codes + (size_t)r * K + (size_t)kb * MX_BLOCK);
+  dst[0] = u32x4_t{w[0], w[1], w[2], w[3]};
+  dst[1] = u32x4_t{w[4], w[5], w[6], w[7]};
+  scales[mx_scale_index(r, kb, K)] = (uint8_t)(e + 127);
+}
+
 }  // namespace
+
+hipError_t launch_mx_quantize_gather(const float* src, int mode, int rows, int C, int cp, int F,
+                                     uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if ((mode != PACK_CONV && mode != PACK_CONV_OUT) || cp < C || cp % 128 || F <= 0 ||
+      ((size_t)codes & 15))
+    return hipErrorInvalidValue;
+  const long K = (long)(mode == PACK_CONV ? 9 : F) * cp;
+  const long n = ((long)rows + 15) / 16 * 16 * (K / MX_BLOCK);
+  hipLaunchKernelGGL(mx_quantize_gather_kernel, dim3((unsigned)((n + MXQ_THREADS - 1) / MXQ_THREADS)),
+                     dim3(MXQ_THREADS), 0, s, src, mode, rows, C, cp, F, codes, scales);
+  return hipGetLastError();
+}
 
 size_t mx_scale_bytes(long rows, int K) { return (size_t)((rows + 15) / 16) * 16 * (size_t)(K / MX_BLOCK); }
 

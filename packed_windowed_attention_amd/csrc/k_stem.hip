@@ -36,11 +36,32 @@ __device__ __forceinline__ void store8<float>(float* p, const float (&v)[8]) {
   reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// MX-fp8 store of a thread's 8 channels: a 32-channel block is 4 consecutive
+// lanes (8-channel groups 4b .. 4b + 3), so its maximum takes two shuffles;
+// the block's first lane writes the scale.
+__device__ __forceinline__ void store8_mx(uint8_t* p, uint8_t* sc, const float (&v)[8], int cg) {
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[k]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  const int e = mx_exponent(amax);
+  *reinterpret_cast<u32x2_t*>(p) =
+      u32x2_t{pack_fp8x4(mx_scale_down(v[0], e), mx_scale_down(v[1], e), mx_scale_down(v[2], e),
+                         mx_scale_down(v[3], e)),
+              pack_fp8x4(mx_scale_down(v[4], e), mx_scale_down(v[5], e), mx_scale_down(v[6], e),
+                         mx_scale_down(v[7], e))};
+  if ((cg & 3) == 0) sc[cg >> 2] = (uint8_t)(e + 127);
+}
+
+// T = uint8_t: MX-fp8 output, cp channels per pixel (channels past C zero),
+// scales row-major cp / 32 bytes per pixel in a1s.
 template <typename T>
 __global__ __launch_bounds__(CONV1_THREADS) void conv1_kernel(
     const float* __restrict__ feat, int T_max, int mel, const int* __restrict__ chunks,
     int chunk_first, const float* __restrict__ w1, const float* __restrict__ b1,
-    T* __restrict__ a1, int C, int cf, int h1, int w1out) {
+    T* __restrict__ a1, int C, int cf, int h1, int w1out, uint8_t* __restrict__ a1s, int cp) {
+  constexpr bool MX = sizeof(T) == 1;
   __shared__ float img[2 * CONV1_ROWS + 1][MAX_CF + 2];
   const int oy0 = blockIdx.x * CONV1_ROWS;
   const int cl = blockIdx.y;  // chunk within the batch
@@ -60,7 +81,8 @@ __global__ __launch_bounds__(CONV1_THREADS) void conv1_kernel(
   }
   __syncthreads();
 
-  const int groups = C >> 3;                     // 8-channel groups
+  const int cs = MX ? cp : C;                    // channels stored per pixel
+  const int groups = cs >> 3;                    // 8-channel groups
   const int xlanes = CONV1_THREADS / groups;     // threads per group
   const int cg = tid % groups;
   const int xl = tid / groups;
@@ -69,9 +91,10 @@ __global__ __launch_bounds__(CONV1_THREADS) void conv1_kernel(
   float w[8][9], bias[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    bias[k] = b1[c0 + k];
+    const bool real = !MX || c0 + k < C;         // padding channels: zero weights and bias
+    bias[k] = real ? b1[c0 + k] : 0.f;
 #pragma unroll
-    for (int t = 0; t < 9; ++t) w[k][t] = w1[(c0 + k) * 9 + t];
+    for (int t = 0; t < 9; ++t) w[k][t] = real ? w1[(c0 + k) * 9 + t] : 0.f;
   }
   const int rows = min(CONV1_ROWS, h1 - oy0);
   for (int item = xl; item < rows * w1out; item += xlanes) {
@@ -90,7 +113,12 @@ __global__ __launch_bounds__(CONV1_THREADS) void conv1_kernel(
       for (int t = 0; t < 9; ++t) a = fmaf(w[k][t], x[t], a);
       v[k] = gelu_f(a);
     }
-    store8<T>(a1 + (((size_t)cl * h1 + oy0 + ry) * w1out + ox) * C + c0, v);
+    const size_t pix = ((size_t)cl * h1 + oy0 + ry) * w1out + ox;
+    if constexpr (MX) {
+      store8_mx(reinterpret_cast<uint8_t*>(a1) + pix * cs + c0, a1s + pix * (cs >> 5), v, cg);
+    } else {
+      store8<T>(a1 + pix * C + c0, v);
+    }
   }
 }
 
@@ -142,16 +170,25 @@ __global__ void pe_kernel(float* pe, int rows, int d) {
 
 hipError_t launch_conv1(const float* feat, int T_max, const int* chunks, int chunk_first, int nb,
                         const float* w1, const float* b1, void* a1, aut_dtype dt,
-                        const Geometry& g, hipStream_t s) {
+                        const Geometry& g, hipStream_t s, uint8_t* a1_scales, int cp) {
   if (nb <= 0) return hipSuccess;
   if (g.cf > MAX_CF || (g.C & 7) || (g.C >> 3) > CONV1_THREADS) return hipErrorInvalidValue;
   dim3 grid((g.h1 + CONV1_ROWS - 1) / CONV1_ROWS, nb);
-  if (dt == AUT_BF16)
+  if (dt == AUT_FP8) {
+    // whole 32-channel blocks in aligned lane quads, at least one thread per group
+    if (cp < g.C || cp % 128 || (cp >> 3) > CONV1_THREADS || !a1_scales) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(conv1_kernel<uint8_t>, grid, dim3(CONV1_THREADS), 0, s, feat, T_max, g.mel,
+                       chunks, chunk_first, w1, b1, (uint8_t*)a1, g.C, g.cf, g.h1, g.w1, a1_scales,
+                       cp);
+  } else if (dt == AUT_BF16) {
     hipLaunchKernelGGL(conv1_kernel<bf16_t>, grid, dim3(CONV1_THREADS), 0, s, feat, T_max, g.mel,
-                       chunks, chunk_first, w1, b1, (bf16_t*)a1, g.C, g.cf, g.h1, g.w1);
-  else
+                       chunks, chunk_first, w1, b1, (bf16_t*)a1, g.C, g.cf, g.h1, g.w1,
+                       (uint8_t*)nullptr, 0);
+  } else {
     hipLaunchKernelGGL(conv1_kernel<float>, grid, dim3(CONV1_THREADS), 0, s, feat, T_max, g.mel,
-                       chunks, chunk_first, w1, b1, (float*)a1, g.C, g.cf, g.h1, g.w1);
+                       chunks, chunk_first, w1, b1, (float*)a1, g.C, g.cf, g.h1, g.w1,
+                       (uint8_t*)nullptr, 0);
+  }
   return hipGetLastError();
 }
 

@@ -233,10 +233,10 @@ def test_inject_argument_checks_before_launch():
 
 def test_fp8_config_default_and_range():
     c = aut.config()
-    assert c.fp8_gemms == aut.FP8_ALL == 31
+    assert c.fp8_gemms == aut.FP8_ALL == 63
     aut.config_check(aut.config(fp8_gemms=0))
     with pytest.raises(aut.AutError) as e:
-        aut.config_check(aut.config(fp8_gemms=32))
+        aut.config_check(aut.config(fp8_gemms=64))
     assert e.value.status == 1
 
 
@@ -253,7 +253,7 @@ def test_fp8_weight_bytes_follow_the_mask():
     d, F, O = cfg_d["d_model"], cfg_d["encoder_ffn_dim"], cfg_d["output_dim"]
     L = cfg_d["encoder_layers"]
     bf = aut.weights_bytes(aut.config(cfg_d), "bf16")
-    full = aut.weights_bytes(aut.config(cfg_d, fp8_gemms=aut.FP8_ALL), "fp8")
+    full = aut.weights_bytes(aut.config(cfg_d, fp8_gemms=aut.FP8_ALL & ~aut.FP8_CONV), "fp8")
     none = aut.weights_bytes(aut.config(cfg_d, fp8_gemms=0), "fp8")
     assert none == bf
     # each fp8 weight: 1 byte + 1/32 of a scale byte per element instead of 2 bytes
@@ -261,6 +261,26 @@ def test_fp8_weight_bytes_follow_the_mask():
     elems = L * per_layer + d * d + O * d
     saved = bf - full
     assert abs(saved - elems * (1 - 1 / 32)) < 256 * (6 * L + 4)   # up to 256-byte alignment per array
+
+
+def test_fp8_conv_weight_bytes():
+    # conv2 / conv3 [C][9 cp] and conv_out [d][16 cp] codes, cp = C rounded up to 128
+    cfg_d = si.model_config("wide")
+    C, d = cfg_d["downsample_hidden_size"], cfg_d["d_model"]
+    cp = (C + 127) // 128 * 128
+    a = aut.weights_bytes(aut.config(cfg_d, fp8_gemms=aut.FP8_ALL), "fp8")
+    b = aut.weights_bytes(aut.config(cfg_d, fp8_gemms=aut.FP8_ALL & ~aut.FP8_CONV), "fp8")
+    conv_bf16 = (2 * C * 9 * C + d * 16 * C) * 2
+    conv_f8 = (2 * C * 9 * cp + d * 16 * cp) * (1 + 1 / 32)
+    assert abs((b - a) - (conv_bf16 - conv_f8)) < 256 * 8
+
+
+def test_fp8_conv_needs_32_channel_blocks():
+    cfg_d = dict(si.model_config("tiny"), downsample_hidden_size=40)
+    with pytest.raises(aut.AutError) as e:
+        aut.weights_bytes(aut.config(cfg_d, fp8_gemms=aut.FP8_ALL), "fp8")
+    assert e.value.status == 2
+    aut.weights_bytes(aut.config(cfg_d, fp8_gemms=aut.FP8_ALL & ~aut.FP8_CONV), "fp8")
 
 
 def test_fp8_needs_128_multiples():

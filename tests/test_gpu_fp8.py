@@ -132,7 +132,7 @@ def check_fp8(g, ref_q, ref, what):
     return cr
 
 
-@pytest.mark.parametrize("mask", [1, 2, 4, 8, 16, 31])
+@pytest.mark.parametrize("mask", [1, 2, 4, 8, 16, 32, 63])
 def test_small_fp8_masks(mask):
     """Each product class alone and all of them, small ragged configuration."""
     cfg_d, lens, feats, P = fp8_case(mask)
@@ -154,21 +154,21 @@ def test_fp8_mask_zero_is_bf16_bitwise():
 def test_rag_fp8():
     """4 ragged requests, 18 layers d 1024, all products MX-fp8: whole output."""
     cfg_d, lens, feats, P = workload("rag")
-    cfg_d = dict(cfg_d, dtype="fp8", fp8_gemms=31)
+    cfg_d = dict(cfg_d, dtype="fp8", fp8_gemms=63)
     print("case: rag fp8 (all products)", flush=True)
     y, _ = forward(cfg_d, lens, feats, P)
-    ref_q, _ = oracle.forward(feats, lens, P, cfg_d, fp8=31)
+    ref_q, _ = oracle.forward(feats, lens, P, cfg_d, fp8=63)
     ref, _ = oracle.forward(feats, lens, P, cfg_d)
     check_fp8(y, ref_q, ref, "rag fp8")
 
 
-@pytest.mark.parametrize("mask", [31, 1])
+@pytest.mark.parametrize("mask", [63, 33])
 def test_wide_fp8_sampled_windows(mask):
     """Full-width workload (24 layers, d 1280) under AUT_FP8, sampled windows.
-    mask 1 (the q/k/v projection only) meets the pages' cosine > 0.999 (mean
-    over tokens) against the unquantized encoder; every product on MX-fp8 does
-    not (e4m3 keeps 3 mantissa bits: about 7e-4 of cosine per product) and is
-    reported."""
+    mask 33 (the conv stem and the q/k/v projection) meets the pages' cosine
+    > 0.999 (mean over tokens) against the unquantized encoder; every product
+    on MX-fp8 does not (e4m3 keeps 3 mantissa bits: about 7e-4 of cosine per
+    layer product) and is reported."""
     cfg_d, lens, feats, P = workload("wide")
     cfg_d = dict(cfg_d, dtype="fp8", fp8_gemms=mask)
     print(f"case: wide fp8 mask {mask}, sampled windows", flush=True)
@@ -185,5 +185,5 @@ def test_wide_fp8_sampled_windows(mask):
         cos.append(check_fp8(g, ref_q, res[w][1], f"wide mask {mask} window {w}"))
     cos = np.concatenate(cos)
     print(f"[wide mask {mask}] vs unquantized: mean cos {cos.mean():.6f} min {cos.min():.6f}", flush=True)
-    if mask == 1:
+    if mask == 33:
         assert cos.mean() > PAGE_COS
