@@ -37,14 +37,25 @@ __device__ __forceinline__ void store8<float>(float* p, const float (&v)[8]) {
 }
 
 // MX-fp8 store of a thread's 8 channels: a 32-channel block is 4 consecutive
-// lanes (8-channel groups 4b .. 4b + 3), so its maximum takes two shuffles;
+// lanes (8-channel groups 4b .. 4b + 3), so its maximum is a quad maximum;
 // the block's first lane writes the scale.
+// Maximum over the 4 lanes of an aligned lane quad: two DPP quad permutes
+// (lane i ^ 1, then lane i ^ 2), vector-ALU moves with no LDS round trip.
+__device__ __forceinline__ float quad_max(float x) {
+  constexpr int XOR1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);  // quad_perm [1, 0, 3, 2]
+  constexpr int XOR2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);  // quad_perm [2, 3, 0, 1]
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), XOR1,
+                                                                  0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), XOR2,
+                                                                  0xF, 0xF, false)));
+  return x;
+}
+
 __device__ __forceinline__ void store8_mx(uint8_t* p, uint8_t* sc, const float (&v)[8], int cg) {
   float amax = 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[k]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  amax = quad_max(amax);
   const int e = mx_exponent(amax);
   *reinterpret_cast<u32x2_t*>(p) =
       u32x2_t{pack_fp8x4(mx_scale_down(v[0], e), mx_scale_down(v[1], e), mx_scale_down(v[2], e),
@@ -96,10 +107,17 @@ __global__ __launch_bounds__(CONV1_THREADS) void conv1_kernel(
 #pragma unroll
     for (int t = 0; t < 9; ++t) w[k][t] = real ? w1[(c0 + k) * 9 + t] : 0.f;
   }
+  // Output pixels of the workgroup are consecutive in memory (item = ry *
+  // w1out + ox), so the store address steps by xlanes pixels per item and only
+  // the LDS position needs (ry, ox), advanced without a division.
   const int rows = min(CONV1_ROWS, h1 - oy0);
-  for (int item = xl; item < rows * w1out; item += xlanes) {
-    const int ry = item / w1out;
-    const int ox = item - ry * w1out;
+  const int n_items = rows * w1out;
+  const size_t pix_first = ((size_t)cl * h1 + oy0) * w1out + xl;
+  int ry = xl / w1out, ox = xl - ry * w1out;   // position of the current item
+  const int dry = xlanes / w1out, dox = xlanes - dry * w1out;
+  T* out = a1 + pix_first * cs + c0;           // (cs bytes per pixel when T is a byte)
+  uint8_t* osc = MX ? a1s + pix_first * (cs >> 5) : nullptr;
+  for (int item = xl; item < n_items; item += xlanes) {
     float x[9];
 #pragma unroll
     for (int kh = 0; kh < 3; ++kh)
@@ -113,11 +131,18 @@ __global__ __launch_bounds__(CONV1_THREADS) void conv1_kernel(
       for (int t = 0; t < 9; ++t) a = fmaf(w[k][t], x[t], a);
       v[k] = gelu_f(a);
     }
-    const size_t pix = ((size_t)cl * h1 + oy0 + ry) * w1out + ox;
     if constexpr (MX) {
-      store8_mx(reinterpret_cast<uint8_t*>(a1) + pix * cs + c0, a1s + pix * (cs >> 5), v, cg);
+      store8_mx(reinterpret_cast<uint8_t*>(out), osc, v, cg);
+      osc += (size_t)xlanes * (cs >> 5);
     } else {
-      store8<T>(a1 + pix * C + c0, v);
+      store8<T>(out, v);
+    }
+    out += (size_t)xlanes * cs;
+    ox += dox;
+    ry += dry;
+    if (ox >= w1out) {
+      ox -= w1out;
+      ++ry;
     }
   }
 }
