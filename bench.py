@@ -305,7 +305,8 @@ def main():
     args = ap.parse_args()
     if args.traffic_summary:
         cmds = [f"rocprofv3 --pmc {c} -f csv -d <out> -o wide -- python <repo>/bench.py --steps 1 --warmup 0 "
-                "--no-cpu-baseline --no-kernel-events" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+                "--no-cpu-baseline --no-kernel-events --fp8-steps 0 --stream-steps 0"
+                for c in ("FETCH_SIZE", "WRITE_SIZE")]
         cmds += [f"rocprofv3 --pmc {c} -f csv -d <out> -o copy -- python <repo>/bench.py --calibrate-copy "
                  f"{args.calibrate_mib}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
         cmds += ["python <repo>/bench.py --traffic-summary <fetch csv> <write csv> <copy fetch csv> <copy write csv>"]
