@@ -151,7 +151,7 @@ def logmel_rate(aut, torch, frame_lens, reps=10):
     return {"frames": int(frames), "audio_seconds": frames / 100.0, "ms": ms,
             "audio_s_per_s": frames / 100.0 / (ms * 1e-3), "tflops": flops / (ms * 1e-3) / 1e12,
             "peak_tflops": PEAK_FP32_TFLOPS, "frac": flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
-            "note": "wall time per call incl. the length upload and one stream sync"}
+            "note": "wall time per call over back-to-back calls, incl. the length upload"}
 
 
 def inject_rate(aut, torch, out, reps=20):
@@ -203,8 +203,8 @@ def stream_latency(aut, torch, cfg, packed, dtype, feats, steps, append=100):
     return {"append_frames": append, "steps": steps, "request_seconds": total / 100.0,
             "step_ms_p50": float(np.percentile(t, 50)), "step_ms_p95": float(np.percentile(t, 95)),
             "rtf_p50": float(np.percentile(t, 50)) / (1e3 * append / 100.0),
-            "note": "wall time per step incl. plan upload and one stream sync; one request, "
-                    "re-encodes at most one 8 s window plus the new chunks"}
+            "note": "wall time per step from an idle stream to its end, incl. the plan upload; one "
+                    "request, re-encodes at most one 8 s window plus the new chunks"}
 
 
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 (MX-fp8) matrix peak
