@@ -1,8 +1,11 @@
 // LayerNorm with bias (cubic.dev wiki, "Transformer Encoder Layers": the
 // encoder uses LayerNorm with bias, not RMSNorm) over fp32 rows, written as
-// the next GEMM's operand type.  One wavefront per row; the row stays in
-// registers, the statistics are fp32 two-pass (mean, then the mean of squared
-// deviations), so the result does not depend on the launch shape.
+// the next GEMM's operand type.  A wavefront takes one row at a time (rows
+// strided over the grid); the row stays in registers, the statistics are fp32
+// two-pass (mean, then the mean of squared deviations), so the result does not
+// depend on the launch shape.
+#include <algorithm>
+
 #include "aut_internal.h"
 #include "device_common.h"
 
@@ -11,15 +14,13 @@ namespace aut {
 namespace {
 
 constexpr int LN_WAVES = 4;
-constexpr int LN_MAXV = 8;  // float4 per lane: d <= 2048
-constexpr int LN_RPW = 1;   // rows per wave (2 or 4 measured slower)
+constexpr int LN_MAXV = 8;            // float4 per lane: d <= 2048
+constexpr int LN_GRID_CAP = 256 * 4;  // workgroups: 16 waves per CU, each over several rows
 
-// butterfly sums over the wavefront of LN_RPW independent values at once
-__device__ __forceinline__ void wave_sum_n(float (&v)[LN_RPW]) {
+// butterfly sum over the wavefront
+__device__ __forceinline__ void wave_sum_n(float (&v)[1]) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1)
-#pragma unroll
-    for (int k = 0; k < LN_RPW; ++k) v[k] += __shfl_xor(v[k], o, 64);
+  for (int o = 32; o >= 1; o >>= 1) v[0] += __shfl_xor(v[0], o, 64);
 }
 
 // four consecutive outputs in one store (8 bytes bf16, 16 bytes fp32)
@@ -46,80 +47,112 @@ __device__ __forceinline__ void store_row4_mx(uint8_t* yr, uint8_t* sc, int row,
   if ((c & 7) == 0) sc[mx_scale_index(row, c >> 3, d)] = (uint8_t)(x + 127);
 }
 
-template <typename T>
+// V float4 per lane (d <= 256 V).  Rows are strided over the grid's waves; a
+// wave loads its next row before it reduces the current one, so that row's
+// loads are in flight during the reductions and stores, and the gain and shift
+// stay in registers for all its rows.
+template <typename T, int V>
 __global__ __launch_bounds__(64 * LN_WAVES) void ln_kernel(const float* __restrict__ x,
                                                           const float* __restrict__ g,
                                                           const float* __restrict__ b,
                                                           T* __restrict__ y, int rows, int d,
                                                           float eps, uint8_t* __restrict__ ysc) {
-  // LN_RPW rows per wave, loaded together so that their loads and their
-  // reductions overlap
   const int lane = threadIdx.x & 63;
-  const int row0 = (blockIdx.x * LN_WAVES + (threadIdx.x >> 6)) * LN_RPW;
-  if (row0 >= rows) return;
+  const int w0 = blockIdx.x * LN_WAVES + (threadIdx.x >> 6);
+  const int nw = gridDim.x * LN_WAVES;
+  if (w0 >= rows) return;
   const int nv = d >> 2;
-  float4 v[LN_RPW][LN_MAXV];
-#pragma unroll
-  for (int k = 0; k < LN_RPW; ++k) {
-    const float4* xr = reinterpret_cast<const float4*>(x + (size_t)(row0 + k) * d);
-    const bool live = row0 + k < rows;
-#pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
-      const int c = lane + 64 * i;
-      v[k][i] = (live && c < nv) ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-  float mean[LN_RPW], rstd[LN_RPW];
-#pragma unroll
-  for (int k = 0; k < LN_RPW; ++k) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) s += (v[k][i].x + v[k][i].y) + (v[k][i].z + v[k][i].w);
-    mean[k] = s;
-  }
-  wave_sum_n(mean);
-#pragma unroll
-  for (int k = 0; k < LN_RPW; ++k) {
-    mean[k] /= (float)d;
-    float q = 0.f;
-#pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
-      const int c = lane + 64 * i;
-      if (c < nv) {
-        const float a0 = v[k][i].x - mean[k], a1 = v[k][i].y - mean[k];
-        const float a2 = v[k][i].z - mean[k], a3 = v[k][i].w - mean[k];
-        q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
-      }
-    }
-    rstd[k] = q;
-  }
-  wave_sum_n(rstd);
   const float4* g4 = reinterpret_cast<const float4*>(g);
   const float4* b4 = reinterpret_cast<const float4*>(b);
+  float4 gg[V], bb[V];
 #pragma unroll
-  for (int k = 0; k < LN_RPW; ++k) {
-    if (row0 + k >= rows) break;
-    const float rs = rsqrtf(rstd[k] / (float)d + eps);
-    T* yr = y + (size_t)(row0 + k) * d;
+  for (int i = 0; i < V; ++i) {
+    const int c = lane + 64 * i;
+    gg[i] = c < nv ? g4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    bb[i] = c < nv ? b4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  auto load_row = [&](float4 (&v)[V], int row) __attribute__((always_inline)) {
+    const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * d);
 #pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
+    for (int i = 0; i < V; ++i) {
+      const int c = lane + 64 * i;
+      v[i] = c < nv ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  float4 v[V];
+  load_row(v, w0);
+  for (int row = w0; row < rows; row += nw) {
+    const int nrow = row + nw;
+    float4 nx[V];
+    if (nrow < rows) load_row(nx, nrow);
+    float mean[1], q[1];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    mean[0] = s;
+    wave_sum_n(mean);
+    const float mu = mean[0] / (float)d;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nv) {
+        const float a0 = v[i].x - mu, a1 = v[i].y - mu;
+        const float a2 = v[i].z - mu, a3 = v[i].w - mu;
+        ss += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+      }
+    }
+    q[0] = ss;
+    wave_sum_n(q);
+    const float rs = rsqrtf(q[0] / (float)d + eps);
+    T* yr = y + (size_t)row * d;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
       const int c = lane + 64 * i;
       if (64 * i >= nv) break;  // uniform: the row's last float4 lies in an earlier i
       const bool live = c < nv;
       float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
       if (live) {
-        const float4 gg = g4[c], bb = b4[c];
-        o0 = (v[k][i].x - mean[k]) * rs * gg.x + bb.x;
-        o1 = (v[k][i].y - mean[k]) * rs * gg.y + bb.y;
-        o2 = (v[k][i].z - mean[k]) * rs * gg.z + bb.z;
-        o3 = (v[k][i].w - mean[k]) * rs * gg.w + bb.w;
+        o0 = (v[i].x - mu) * rs * gg[i].x + bb[i].x;
+        o1 = (v[i].y - mu) * rs * gg[i].y + bb[i].y;
+        o2 = (v[i].z - mu) * rs * gg[i].z + bb[i].z;
+        o3 = (v[i].w - mu) * rs * gg[i].w + bb[i].w;
       }
       if constexpr (sizeof(T) == 1) {
-        store_row4_mx(reinterpret_cast<uint8_t*>(yr), ysc, row0 + k, c, d, o0, o1, o2, o3, live);
+        store_row4_mx(reinterpret_cast<uint8_t*>(yr), ysc, row, c, d, o0, o1, o2, o3, live);
       } else if (live) {
         store_row4(yr + 4 * c, o0, o1, o2, o3);
       }
     }
+    if (nrow < rows) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) v[i] = nx[i];
+    }
+  }
+}
+
+template <typename T, int V>
+hipError_t run_ln(const float* x, const float* g, const float* b, T* y, int T_rows, int d, float eps,
+                  uint8_t* ysc, hipStream_t s) {
+  const int wgs = std::min((T_rows + LN_WAVES - 1) / LN_WAVES, LN_GRID_CAP);
+  hipLaunchKernelGGL((ln_kernel<T, V>), dim3(wgs), dim3(64 * LN_WAVES), 0, s, x, g, b, y, T_rows, d,
+                     eps, ysc);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t run_ln_any(const float* x, const float* g, const float* b, T* y, int T_rows, int d,
+                      float eps, uint8_t* ysc, hipStream_t s) {
+  switch ((d / 4 + 63) / 64) {
+    case 1: return run_ln<T, 1>(x, g, b, y, T_rows, d, eps, ysc, s);
+    case 2: return run_ln<T, 2>(x, g, b, y, T_rows, d, eps, ysc, s);
+    case 3: return run_ln<T, 3>(x, g, b, y, T_rows, d, eps, ysc, s);
+    case 4: return run_ln<T, 4>(x, g, b, y, T_rows, d, eps, ysc, s);
+    case 5: return run_ln<T, 5>(x, g, b, y, T_rows, d, eps, ysc, s);
+    case 6: return run_ln<T, 6>(x, g, b, y, T_rows, d, eps, ysc, s);
+    case 7: return run_ln<T, 7>(x, g, b, y, T_rows, d, eps, ysc, s);
+    case 8: return run_ln<T, 8>(x, g, b, y, T_rows, d, eps, ysc, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -129,19 +162,12 @@ hipError_t launch_layernorm(const float* x, const float* g, const float* b, void
                             float eps, aut_dtype dt, hipStream_t s, uint8_t* y_scales) {
   if (T <= 0) return hipSuccess;
   if (d % 4 || d > 4 * 64 * LN_MAXV) return hipErrorInvalidValue;
-  dim3 grid((T + LN_WAVES * LN_RPW - 1) / (LN_WAVES * LN_RPW));
   if (dt == AUT_FP8) {
     if (d % 128 || !y_scales) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(ln_kernel<uint8_t>, grid, dim3(64 * LN_WAVES), 0, s, x, g, b, (uint8_t*)y,
-                       T, d, eps, y_scales);
-  } else if (dt == AUT_BF16) {
-    hipLaunchKernelGGL(ln_kernel<bf16_t>, grid, dim3(64 * LN_WAVES), 0, s, x, g, b, (bf16_t*)y, T,
-                       d, eps, (uint8_t*)nullptr);
-  } else {
-    hipLaunchKernelGGL(ln_kernel<float>, grid, dim3(64 * LN_WAVES), 0, s, x, g, b, (float*)y, T, d,
-                       eps, (uint8_t*)nullptr);
+    return run_ln_any<uint8_t>(x, g, b, (uint8_t*)y, T, d, eps, y_scales, s);
   }
-  return hipGetLastError();
+  if (dt == AUT_BF16) return run_ln_any<bf16_t>(x, g, b, (bf16_t*)y, T, d, eps, nullptr, s);
+  return run_ln_any<float>(x, g, b, (float*)y, T, d, eps, nullptr, s);
 }
 
 }  // namespace aut
