@@ -46,6 +46,19 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _check_launch_stubs(lib: str) -> None:
+    """Every kernel the host code launches has its launch stub in the library.
+    (The host compilation pass can leave a kernel template's stubs undefined
+    without a diagnostic; the library would then fail only when loaded.)"""
+    r = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"nm failed on {lib}:\n{r.stderr}")
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        os.unlink(lib)
+        raise RuntimeError("kernel launch stubs missing from the library: " + ", ".join(missing[:8]))
+
+
 def build(verbose: bool = False) -> str:
     """Compiles every source and links libaut.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -57,6 +70,7 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
+    _check_launch_stubs(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -76,7 +76,70 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Epilogue through LDS.  A lane's accumulators cover 4 consecutive columns of
+// Implicit 3x3 stride-2 pad-1 convolution over a channels-last activation
+// (openarchlab "1A", section 3: Conv2d(k=3, s=2, p=1)), k = tap * cin + c.
+// Per load row: the byte offset of its window's tap-(0, 0) pixel, channel 0
+// (negative when that corner lies in the padding), and a 9-bit mask of the
+// taps that fall inside the image (no bit for rows past M).  Per lane: the tap
+// and channel of its 16-byte unit at the current k step, advanced one step per
+// issue, so a load's offset is a bit test and an add.  Taps past the ninth
+// (the k tail) have no bit and load zero.  Kernels declare it full size in
+// every A mode: with a one-row instance, the constant out-of-range indices in
+// the mode's dead branches made the host compilation pass drop the kernels'
+// launch stubs without a diagnostic.
+template <int NL, int ES>
+struct ConvGather {
+  int base[NL];
+  unsigned valid[NL];
+  int tap, ci;
+  __host__ __device__ __forceinline__ void row(const GemmArgs& p, int j, int m) {
+    base[j] = 0;
+    valid[j] = 0u;
+    if (m >= p.M) return;
+    const int hw = p.hout * p.wout;
+    const int chunk = m / hw;
+    const int rem = m - chunk * hw;
+    int oy, ox;
+    if (p.xmajor) {
+      ox = rem / p.hout;
+      oy = rem - ox * p.hout;
+    } else {
+      oy = rem / p.wout;
+      ox = rem - oy * p.wout;
+    }
+    base[j] = (chunk * p.hin * p.win + (2 * oy - 1) * p.win + (2 * ox - 1)) * p.cin * ES;
+    unsigned v = 0u;
+#pragma unroll
+    for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+      for (int kw = 0; kw < 3; ++kw) {
+        const int iy = 2 * oy + kh - 1, ix = 2 * ox + kw - 1;
+        if (iy >= 0 && iy < p.hin && ix >= 0 && ix < p.win) v |= 1u << (3 * kh + kw);
+      }
+    valid[j] = v;
+  }
+  __host__ __device__ __forceinline__ void start(int k0, int cin) {
+    tap = k0 / cin;
+    ci = k0 - tap * cin;
+  }
+  __host__ __device__ __forceinline__ void advance(int bk, int cin) {
+    ci += bk;
+    while (ci >= cin) {
+      ci -= cin;
+      ++tap;
+    }
+  }
+  __host__ __device__ __forceinline__ int tap_offset(const GemmArgs& p) const {
+    const int kh = (tap * 11) >> 5;  // tap / 3 for the taps that matter (0..10)
+    const int kw = tap - 3 * kh;
+    return ((kh * p.win + kw) * p.cin + ci) * ES;
+  }
+  __host__ __device__ __forceinline__ unsigned offset(int j, int toff) const {
+    return ((valid[j] >> tap) & 1u) ? (unsigned)(base[j] + toff) : OOB;
+  }
+};
+
+// Epilogue through LDS.// Epilogue through LDS.  A lane's accumulators cover 4 consecutive columns of
 // scattered rows, so storing them straight to memory writes 8- or 16-byte
 // pieces of many cache lines, which the memory system then writes back as
 // partial lines.  Instead the tile goes through LDS (the operand stages are
@@ -299,9 +362,9 @@ void gemm256_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   // Rows past M give offsets past a_bytes and load zero.
   const unsigned a_step = (unsigned)(32 * p.lda * 2);
   const unsigned a_off0 = (unsigned)((wave * 8 + lrow8) * p.lda * 2);
-  // A_ROWMAP: per-load row offsets; A_CONV: per-load chunk offset and pixel
-  unsigned a_rowoff[AMODE == A_PLAIN ? 1 : A_LOADS];
-  int a_pix[AMODE == A_CONV ? A_LOADS : 1];  // (oy << 16) | ox, or -1 past M
+  // A_ROWMAP: per-load row offsets; A_CONV: per-load window corners and taps
+  unsigned a_rowoff[A_LOADS];
+  ConvGather<A_LOADS, 2> cg;  // (full size in every mode: see ConvGather)
   if (AMODE != A_PLAIN) {
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
@@ -309,25 +372,10 @@ void gemm256_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
       if (AMODE == A_ROWMAP) {
         a_rowoff[j] = m < M ? (unsigned)((size_t)(p.rowmap[m] - p.rowmap_base) * p.lda * 2) : OOB;
       } else {
-        a_rowoff[j] = 0;
-        a_pix[j] = -1;
-        if (m < M) {
-          const int hw = p.hout * p.wout;
-          const int chunk = m / hw;
-          const int rem = m - chunk * hw;
-          int oy, ox;
-          if (p.xmajor) {
-            ox = rem / p.hout;
-            oy = rem - ox * p.hout;
-          } else {
-            oy = rem / p.wout;
-            ox = rem - oy * p.wout;
-          }
-          a_pix[j] = (oy << 16) | ox;
-          a_rowoff[j] = (unsigned)((size_t)chunk * p.hin * p.win * p.cin * 2);
-        }
+        cg.row(p, j, m);
       }
     }
+    if (AMODE == A_CONV) cg.start(lunit * 8, p.cin);
   }
   // B: offset of load j = b_off0 + j * b_step + 2 k; rows past N load zero.
   const char* b_base = (const char*)p.B + (size_t)n0 * p.ldb * 2;
@@ -344,20 +392,12 @@ void gemm256_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
     // k past K: an offset that is past every buffer
     const unsigned koff = k < K ? (unsigned)(2 * k) : OOB;
     if (AMODE == A_CONV) {
-      const int tap = k / p.cin;
-      const int ci = k - tap * p.cin;
-      const int kh = tap / 3;
-      const int kw = tap - 3 * kh;
+      const int toff = cg.tap_offset(p);
 #pragma unroll
-      for (int j = 0; j < A_LOADS; ++j) {
-        const int oy = a_pix[j] >> 16, ox = a_pix[j] & 0xFFFF;
-        const int iy = 2 * oy + kh - 1;
-        const int ix = 2 * ox + kw - 1;
-        const bool ok = a_pix[j] >= 0 && k < K && iy >= 0 && iy < p.hin && ix >= 0 && ix < p.win;
-        const unsigned off = ok ? a_rowoff[j] + (unsigned)(((iy * p.win + ix) * p.cin + ci) * 2) : OOB;
+      for (int j = 0; j < A_LOADS; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(j * 4 + wave) * 64]), 16,
-                                                 off, 0, 0, 0);
-      }
+                                                 cg.offset(j, toff), 0, 0, 0);
+      cg.advance(BK, p.cin);  // steps are issued in increasing order
     } else {
 #pragma unroll
       for (int j = 0; j < A_LOADS; ++j) {
@@ -502,8 +542,8 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   }
   const unsigned a_step = (unsigned)(64 * p.lda * 2);
   const unsigned a_off0 = (unsigned)((wave * 8 + lrow8) * p.lda * 2);
-  unsigned a_rowoff[AMODE == A_PLAIN ? 1 : A_LOADS];
-  int a_pix[AMODE == A_CONV ? A_LOADS : 1];
+  unsigned a_rowoff[A_LOADS];
+  ConvGather<A_LOADS, 2> cg;  // (full size in every mode: see ConvGather)
   if (AMODE != A_PLAIN) {
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
@@ -511,25 +551,10 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
       if (AMODE == A_ROWMAP) {
         a_rowoff[j] = m < M ? (unsigned)((size_t)(p.rowmap[m] - p.rowmap_base) * p.lda * 2) : OOB;
       } else {
-        a_rowoff[j] = 0;
-        a_pix[j] = -1;
-        if (m < M) {
-          const int hw = p.hout * p.wout;
-          const int chunk = m / hw;
-          const int rem = m - chunk * hw;
-          int oy, ox;
-          if (p.xmajor) {
-            ox = rem / p.hout;
-            oy = rem - ox * p.hout;
-          } else {
-            oy = rem / p.wout;
-            ox = rem - oy * p.wout;
-          }
-          a_pix[j] = (oy << 16) | ox;
-          a_rowoff[j] = (unsigned)((size_t)chunk * p.hin * p.win * p.cin * 2);
-        }
+        cg.row(p, j, m);
       }
     }
+    if (AMODE == A_CONV) cg.start(lunit * 8, p.cin);
   }
   const char* b_base = (const char*)p.B + (size_t)n0 * p.ldb * 2;
   const unsigned b_bytes = (unsigned)((size_t)(N - n0) * p.ldb * 2);
@@ -544,20 +569,12 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
     const int k = kt * BK + lunit * 8;
     const unsigned koff = k < K ? (unsigned)(2 * k) : OOB;
     if (AMODE == A_CONV) {
-      const int tap = k / p.cin;
-      const int ci = k - tap * p.cin;
-      const int kh = tap / 3;
-      const int kw = tap - 3 * kh;
+      const int toff = cg.tap_offset(p);
 #pragma unroll
-      for (int j = 0; j < A_LOADS; ++j) {
-        const int oy = a_pix[j] >> 16, ox = a_pix[j] & 0xFFFF;
-        const int iy = 2 * oy + kh - 1;
-        const int ix = 2 * ox + kw - 1;
-        const bool ok = a_pix[j] >= 0 && k < K && iy >= 0 && iy < p.hin && ix >= 0 && ix < p.win;
-        const unsigned off = ok ? a_rowoff[j] + (unsigned)(((iy * p.win + ix) * p.cin + ci) * 2) : OOB;
+      for (int j = 0; j < A_LOADS; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(j * 8 + wave) * 64]), 16,
-                                                 off, 0, 0, 0);
-      }
+                                                 cg.offset(j, toff), 0, 0, 0);
+      cg.advance(BK, p.cin);  // steps are issued in increasing order
     } else {
 #pragma unroll
       for (int j = 0; j < A_LOADS; ++j) {
@@ -698,9 +715,9 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   }
   const unsigned a_step = (unsigned)(64 * p.lda);
   const unsigned a_off0 = (unsigned)((wave * 8 + lrow8) * p.lda);
-  // A_ROWMAP: per-load row offsets; A_CONV: per-load chunk offset and pixel
-  unsigned a_rowoff[AMODE == A_PLAIN ? 1 : A_LOADS];
-  int a_pix[AMODE == A_CONV ? A_LOADS : 1];  // (oy << 16) | ox, or -1 past M
+  // A_ROWMAP: per-load row offsets; A_CONV: per-load window corners and taps
+  unsigned a_rowoff[A_LOADS];
+  ConvGather<A_LOADS, 1> cg;  // (full size in every mode: see ConvGather)
   // output pixel of GEMM row m: {chunk, (oy << 16) | ox}
   auto conv_pixel = [&](int m) __attribute__((always_inline)) {
     const int hw = p.hout * p.wout;
@@ -723,15 +740,10 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
       if (AMODE == A_ROWMAP) {
         a_rowoff[j] = m < M ? (unsigned)((size_t)(p.rowmap[m] - p.rowmap_base) * p.lda) : OOB;
       } else {
-        a_rowoff[j] = 0;
-        a_pix[j] = -1;
-        if (m < M) {
-          const int2 cpx = conv_pixel(m);
-          a_pix[j] = cpx.y;
-          a_rowoff[j] = (unsigned)((size_t)cpx.x * p.hin * p.win * p.cin);
-        }
+        cg.row(p, j, m);
       }
     }
+    if (AMODE == A_CONV) cg.start(lunit * 16, p.cin);
   }
   // (an MX epilogue that writes zero columns past N may run tiles with n0 >= N:
   // their B rows all load zero)
@@ -776,21 +788,12 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   auto issue = [&](int kt, u32x4_t* As_s, u32x4_t* Bs_s, unsigned* Sa_s, unsigned* Sb_s)
       __attribute__((always_inline)) {
     if (AMODE == A_CONV) {
-      const int k = kt * BK8 + lunit * 16;
-      const int tap = k / p.cin;
-      const int ci = k - tap * p.cin;
-      const int kh = tap / 3;
-      const int kw = tap - 3 * kh;
+      const int toff = cg.tap_offset(p);
 #pragma unroll
-      for (int j = 0; j < A_LOADS; ++j) {
-        const int oy = a_pix[j] >> 16, ox = a_pix[j] & 0xFFFF;
-        const int iy = 2 * oy + kh - 1;
-        const int ix = 2 * ox + kw - 1;
-        const bool ok = a_pix[j] >= 0 && iy >= 0 && iy < p.hin && ix >= 0 && ix < p.win;
-        const unsigned off = ok ? a_rowoff[j] + (unsigned)((iy * p.win + ix) * p.cin + ci) : OOB;
+      for (int j = 0; j < A_LOADS; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(j * 8 + wave) * 64]), 16,
-                                                 off, 0, 0, 0);
-      }
+                                                 cg.offset(j, toff), 0, 0, 0);
+      cg.advance(BK8, p.cin);  // steps are issued in increasing order
     } else {
       const unsigned koff = (unsigned)(kt * BK8 + lunit * 16);
 #pragma unroll
