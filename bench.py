@@ -178,6 +178,37 @@ def inject_rate(aut, torch, out, reps=20):
             "peak_gbs": PEAK_HBM_GBS, "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
 
 
+def graph_rate(aut, torch, cfg, pl, fd, packed, dtype, eager_out, steps, audio_s):
+    """The planned forward as a HIP graph: the plan is built and uploaded once,
+    outside; aut_encode_planned (kernels only) is captured once and replayed
+    `steps` times between two synchronisations. The replay's output is checked
+    bit for bit against the eager forward's."""
+    ws = aut.workspace(cfg, pl, dtype)
+    out = torch.full_like(eager_out, float("nan"))
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        aut.plan_upload(pl, ws, stream=side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        aut.encode_planned(cfg, pl, fd, packed, dtype, out, ws, stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out, eager_out))
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / steps
+    T = pl.total_tokens
+    del g, ws
+    return {"ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "audio_s_per_s": audio_s / (ms / 1e3),
+            "replays": steps, "bit_identical_to_eager": same,
+            "note": "aut_encode_planned captured once in a HIP graph, plan built and uploaded once "
+                    "outside; wall time per replay between two synchronisations"}
+
+
 def stream_latency(aut, torch, cfg, packed, dtype, feats, steps, append=100):
     """Incremental encode of one live request (the workload's first request's
     mel, repeated as needed) receiving `append` frames per step: each step
@@ -270,7 +301,7 @@ def cpu_baseline(name, cfg_d, lens, feats, P, n_windows):
     t0 = time.perf_counter()
     oracle.forward_windows(feats, lens, P, cfg_d, wins)
     dt = time.perf_counter() - t0
-    return {
+    res = {
         "value": ntok / dt,
         "unit": "tokens/s",
         "cores": int(threads),
@@ -279,7 +310,32 @@ def cpu_baseline(name, cfg_d, lens, feats, P, n_windows):
                   f"conv stem, conv_out, {cfg_d['encoder_layers']} layers and projector in float64 numpy; "
                   f"{dt:.1f} s wall",
         "audio_s_per_s": ntok / 13.0 / dt,
+        "cpu_model": cpu_model(),
     }
+    # the same oracle on one thread, over the first sampled window only
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        return res
+    w1 = wins[:1]
+    n1 = sum(pl["window_lengths"][w] for w in w1)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.forward_windows(feats, lens, P, cfg_d, w1)
+        d1 = time.perf_counter() - t0
+    res["one_thread"] = {"value": n1 / d1, "unit": "tokens/s",
+                         "sample": f"window {w1[0]} ({n1} tokens), {d1:.1f} s wall"}
+    return res
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -294,6 +350,8 @@ def main():
                     help="steps of the AUT_FP8 legs (0: skip them)")
     ap.add_argument("--stream-steps", type=int, default=30,
                     help="1 s appends timed for the incremental-encode latency (0: skip)")
+    ap.add_argument("--graph-steps", type=int, default=10,
+                    help="replays of the forward captured in a HIP graph (0: skip)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without per-launch HIP events (no roofline)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -454,6 +512,10 @@ def main():
         allf = sum(s["flops"] for c, s in stats.items() if c != "layernorm" and c != "gemm_fp8")
         res["mfma_frac_step"] = allf / args.steps / (ms_per_step / 1e3) / 1e12 / peak
         res["attention_gbs"] = a["bytes"] / (a["total_ms"] / 1e3) / 1e9 if a["total_ms"] else None
+    if args.graph_steps > 0:
+        res["graph_replay"] = graph_rate(aut, torch, cfg, pl, fd, packed, dtype, out, args.graph_steps, audio_s)
+        log(f"graph replay: {res['graph_replay']['ms_per_step']:.3f} ms/step, "
+            f"bit-identical to eager: {res['graph_replay']['bit_identical_to_eager']}")
     res["logmel"] = logmel_rate(aut, torch, lens)
     log(f"logmel: {res['logmel']['ms']:.3f} ms for {res['logmel']['audio_seconds']:.0f} s of audio")
     res["inject"] = inject_rate(aut, torch, out)
