@@ -205,7 +205,7 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& p, int m0, int n
         float v[4] = {av[0] + bq[j].x, av[1] + bq[j].y, av[2] + bq[j].z, av[3] + bq[j].w};
         if (EPI == EPI_STORE_GELU || MX) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = gelu_f(v[r]);
+          for (int r = 0; r < 4; ++r) v[r] = F32 && !MX ? gelu_f(v[r]) : gelu_bf16(v[r]);
         }
         const int col = wn * WN + 16 * j + 4 * g;
         if (F32) {

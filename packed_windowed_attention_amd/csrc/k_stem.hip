@@ -129,7 +129,7 @@ __global__ __launch_bounds__(CONV1_THREADS) void conv1_kernel(
       float a = bias[k];
 #pragma unroll
       for (int t = 0; t < 9; ++t) a = fmaf(w[k][t], x[t], a);
-      v[k] = gelu_f(a);
+      v[k] = sizeof(T) == 4 ? gelu_f(a) : gelu_bf16(a);
     }
     if constexpr (MX) {
       store8_mx(reinterpret_cast<uint8_t*>(out), osc, v, cg);
