@@ -139,7 +139,7 @@ struct ConvGather {
   }
 };
 
-// Epilogue through LDS.// Epilogue through LDS.  A lane's accumulators cover 4 consecutive columns of
+// Epilogue through LDS.  A lane's accumulators cover 4 consecutive columns of
 // scattered rows, so storing them straight to memory writes 8- or 16-byte
 // pieces of many cache lines, which the memory system then writes back as
 // partial lines.  Instead the tile goes through LDS (the operand stages are
@@ -601,15 +601,18 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   const int g = lane >> 4;
   // one step from a stage: wait for this thread's loads of step kt (nothing
   // later is in flight yet), barrier so that every wave's loads have landed
-  // and step kt - 1 is consumed, load step kt + 1 into the other stage, then
-  // the matrix instructions of the two 32-deep halves of the step
+  // and step kt - 1 is consumed, then the matrix instructions of the two
+  // 32-deep halves of the step.  The loads of step kt + 1 into the other stage
+  // go out after the first fragment reads, so that their issue overlaps the
+  // reads' latency; they are unconditional (past the last step every offset
+  // is out of range and they write zeros, waited for before the epilogue) so
+  // that the step stays one block for the scheduler.
   auto step = [&](int kt, const u32x4_t* As_s, const u32x4_t* Bs_s, u32x4_t* As_n, u32x4_t* Bs_n)
       __attribute__((always_inline)) {
     wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + 1 < nk) issue(kt + 1, As_n, Bs_n);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int u = 4 * h + g;
@@ -624,11 +627,13 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
         const int r = wm * 128 + 16 * i + lrow;
         frag_from_units(xa[i], As_s[r * KU + swz(u, r)], zero_unit());
       }
+      if (h == 0) issue(kt + 1, As_n, Bs_n);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < NTW; ++j) mma16_k32(acc[j][i], wb[j], xa[i]);
       __builtin_amdgcn_sched_group_barrier(0x100, NTW + 2, 0);  // DS reads
+      if (h == 0) __builtin_amdgcn_sched_group_barrier(0x020, A_LOADS + B_LOADS, 0);  // loads
 #pragma unroll
       for (int i = 0; i < 6; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, NTW, 0);     // MFMA
@@ -644,6 +649,7 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
     step(kt, As0, Bs0, As1, Bs1);
     if (kt + 1 < nk) step(kt + 1, As1, Bs1, As0, Bs0);
   }
+  wait_vmcnt<0>();  // the zero-filling loads of the step past the last
 
   staged_epilogue<BN, WN, NT8, EPI>(p, m0, n0, wm, wn, tid, acc, As0, As1, Bs0, Bs1);
 }
