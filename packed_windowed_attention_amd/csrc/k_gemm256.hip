@@ -45,6 +45,14 @@ constexpr int BK = 64;      // bf16 per row per k step
 constexpr int GROUP_M = 8;
 constexpr unsigned OOB = 0x80000000u;  // an offset past every buffer here: loads zero
 
+// Record count of a tile's A descriptor (based at the tile's first row): the
+// rest of the matrix, capped at 2^31 bytes.  A tile reads at most BM rows past
+// its base, so the cap never cuts a real access, keeps the count within 32
+// bits for any number of rows, and keeps every offset >= OOB out of range.
+__device__ __forceinline__ unsigned tile_records(size_t bytes) {
+  return bytes < (size_t)OOB ? (unsigned)bytes : OOB;
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int unit, int row) { return unit ^ (row & 7); }
@@ -353,7 +361,7 @@ void gemm256_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   unsigned a_bytes;
   if (AMODE == A_PLAIN) {
     a_base = (const char*)p.A + (size_t)m0 * p.lda * 2;
-    a_bytes = (unsigned)((size_t)(M - m0) * p.lda * 2);
+    a_bytes = tile_records((size_t)(M - m0) * p.lda * 2);
   } else {
     a_base = (const char*)p.A;
     a_bytes = (unsigned)p.a_bytes;
@@ -535,7 +543,7 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   unsigned a_bytes;
   if (AMODE == A_PLAIN) {
     a_base = (const char*)p.A + (size_t)m0 * p.lda * 2;
-    a_bytes = (unsigned)((size_t)(M - m0) * p.lda * 2);
+    a_bytes = tile_records((size_t)(M - m0) * p.lda * 2);
   } else {
     a_base = (const char*)p.A;
     a_bytes = (unsigned)p.a_bytes;
@@ -714,7 +722,7 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   unsigned a_bytes;
   if (AMODE == A_PLAIN) {
     a_base = (const char*)p.A + (size_t)m0 * p.lda;
-    a_bytes = (unsigned)((size_t)(M - m0) * p.lda);
+    a_bytes = tile_records((size_t)(M - m0) * p.lda);
   } else {
     a_base = (const char*)p.A;
     a_bytes = (unsigned)p.a_bytes;

@@ -136,6 +136,51 @@ def test_large_sampled_windows(name):
         check(y[r0:r0 + ref.shape[0]], ref, "bf16", f"{name} window {w} (rows {r0}+{ref.shape[0]})")
 
 
+def wrap_band_windows(T, lda_elems, elem_bytes, cu):
+    """Windows holding rows that a 256-row GEMM tile would lose if its A
+    descriptor took the rest of the matrix, (T - m0) * lda bytes, as a 32-bit
+    count: where that count wraps past 2^32 to less than the tile's own span,
+    the tile's rows beyond the wrapped count read as zero."""
+    row_bytes = lda_elems * elem_bytes
+    rows = []
+    for m0 in range(0, T, 256):
+        rest = (T - m0) * row_bytes
+        if rest >= 1 << 32 and rest % (1 << 32) < 256 * row_bytes:
+            first = m0 + -(-(rest % (1 << 32)) // row_bytes)
+            rows += list(range(first, min(m0 + 256, T)))
+    return sorted({int(np.searchsorted(cu, r, side="right") - 1) for r in rows})
+
+
+def test_max_batch_sampled_windows():
+    """One 35 000 s request, 455 000 tokens in one bf16 batch (13.8 GiB of
+    workspace): past the size where a GEMM tile's A descriptor count, the rest
+    of the matrix in bytes, no longer fits 32 bits (fc2's A is T x 5120 bf16,
+    2^32 bytes at 419 430 rows). The windows of the rows a wrapped count would
+    have cut are recomputed by the oracle, with the first, a middle and the
+    last window; only the sampled rows leave the GPU."""
+    from packed_windowed_attention_amd import aut
+    torch = torch_mod()
+    cfg_d, _, _, P = workload("wide")
+    lens = np.array([3_500_000])
+    feats = si.mel_features(lens, seed=77)
+    opl = oracle.plan(lens, cfg_d)
+    cu = np.asarray(opl["cu_seqlens"])
+    T = int(cu[-1])
+    assert T == 455_000
+    band = wrap_band_windows(T, cfg_d["encoder_ffn_dim"], 2, cu)
+    assert band, "the sample must include rows past a wrap of the 32-bit count"
+    wins = sorted({0, len(cu) // 2, len(cu) - 2} | set(band))
+    print(f"case: max batch bf16, T={T}, windows {wins}", flush=True)
+    cfg, packed = pack(cfg_d, P)
+    out, pl = aut.encode(cfg, features_dev(feats), lens, packed, "bf16")
+    torch.cuda.synchronize()
+    assert pl.copy()[1] == opl["cu_seqlens"]
+    res = oracle.forward_windows(feats, lens, P, cfg_d, wins)
+    for w, (r0, ref) in res.items():
+        g = out[r0:r0 + ref.shape[0]].double().cpu().numpy()
+        check(g, ref, "bf16", f"max batch window {w} (rows {r0}+{ref.shape[0]})")
+
+
 def test_wide_bench_launch_config():
     """The wide workload in the launch configuration bench.py times (conv-stem
     batches as large as the library allows), seeded sample of windows."""
