@@ -26,9 +26,12 @@ namespace {
 constexpr int ATT_THREADS = 256;
 constexpr int LMAX = 128;
 
+// Row pitch of the transposed V in LDS.  Fragment reads take 8 bytes (bf16)
+// or 16 (fp32) from 16 or 8 consecutive rows per 128-byte LDS cycle: a pitch
+// of 8 or 16 bytes past a multiple of 128 puts those rows on distinct banks.
 template <typename T> struct VtStride;
-template <> struct VtStride<bf16_t> { static constexpr int value = LMAX + 8; };
-template <> struct VtStride<float> { static constexpr int value = LMAX + 4; };
+template <> struct VtStride<bf16_t> { static constexpr int value = LMAX + 4; };  // 264 bytes
+template <> struct VtStride<float> { static constexpr int value = LMAX + 4; };   // 528 bytes
 
 template <typename T>
 __device__ __forceinline__ int kswz(int u, int j) {
