@@ -33,6 +33,15 @@ constexpr int LM_SPAN = LM_FRAMES * LM_HOP + LM_NFFT - LM_HOP;  // samples cover
 constexpr int LM_KC = 40;                        // DFT table rows per LDS chunk
 constexpr int LM_TILES = 2 * LM_BIN_TILES;       // cos / sin column tiles
 constexpr int LM_COLS = 16 * LM_TILES;           // 416
+// LDS layouts, padded so that the reads of a 32-lane cycle (16 frames or rows
+// x 2 values of k) fall on distinct banks (32 banks of 4 bytes):
+// the audio span with 2 floats after every hop of 160 samples (a frame starts
+// 162 floats after the previous one: 2 banks on), the DFT table chunk with a
+// row pitch of 432 floats (16 banks on), the power spectrum with 226 (2 on).
+constexpr int LM_SPAN_LDS = LM_SPAN + 2 * (LM_SPAN / LM_HOP + 1);
+constexpr int LM_COLS_LDS = LM_COLS + 16;        // 432
+constexpr int LM_PB_LDS = 16 * LM_BIN_TILES + 18;  // 226
+__device__ __forceinline__ int span_slot(int i) { return i + 2 * (i / LM_HOP); }
 
 // Slaney mel scale (linear 3/200 mel per Hz up to 1 kHz = 15 mel, then 27
 // mel per factor 6.4) and its inverse
@@ -90,9 +99,9 @@ __device__ __forceinline__ f32x4_t mma4(float a, float b, f32x4_t c) {
 __global__ __launch_bounds__(LM_THREADS) void logmel_kernel(
     const float* __restrict__ audio, long s_max, const int* __restrict__ lens, const float* __restrict__ dft,
     const float* __restrict__ melw, float* __restrict__ feat, int T_max, unsigned* __restrict__ mx) {
-  __shared__ float span[LM_SPAN];
-  __shared__ float buf[LM_KC * LM_COLS];  // DFT table chunk, then the power spectrum
-  static_assert(LM_FRAMES * 16 * LM_BIN_TILES <= LM_KC * LM_COLS, "power tile fits");
+  __shared__ float span[LM_SPAN_LDS];
+  __shared__ float buf[LM_KC * LM_COLS_LDS];  // DFT table chunk, then the power spectrum
+  static_assert(LM_FRAMES * LM_PB_LDS <= LM_KC * LM_COLS_LDS, "power tile fits");
   const int b = blockIdx.y;
   const int N = lens[b];
   const int nf = N / LM_HOP;
@@ -107,24 +116,28 @@ __global__ __launch_bounds__(LM_THREADS) void logmel_kernel(
     int s = f0 * LM_HOP - LM_NFFT / 2 + i;
     if (s < 0) s = -s;
     if (s >= N) s = 2 * (N - 1) - s;
-    span[i] = (s >= 0 && s < N) ? x[s] : 0.f;
+    span[span_slot(i)] = (s >= 0 && s < N) ? x[s] : 0.f;
   }
 
   // DFT: acc[t] = 16 frames (this wave's) x 16 columns of tile t
   f32x4_t acc[LM_TILES];
 #pragma unroll
   for (int t = 0; t < LM_TILES; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int frame_off = (16 * wave + lr) * LM_HOP;
+  const int frame_off = (16 * wave + lr) * (LM_HOP + 2);  // span_slot of the frame's first sample
   for (int c = 0; c < LM_NFFT / LM_KC; ++c) {
     __syncthreads();  // the previous chunk is consumed (and the span is in place)
     const float4* src = reinterpret_cast<const float4*>(dft + (long)c * LM_KC * LM_COLS);
-    for (int i = tid; i < LM_KC * LM_COLS / 4; i += LM_THREADS) reinterpret_cast<float4*>(buf)[i] = src[i];
+    for (int i = tid; i < LM_KC * LM_COLS / 4; i += LM_THREADS) {
+      const int row = i / (LM_COLS / 4);
+      reinterpret_cast<float4*>(buf)[i + row * ((LM_COLS_LDS - LM_COLS) / 4)] = src[i];
+    }
     __syncthreads();
 #pragma unroll 2
     for (int kk = 0; kk < LM_KC / 4; ++kk) {
       const int k = 4 * kk + g;
-      const float a = span[frame_off + c * LM_KC + k];
-      const float* brow = buf + k * LM_COLS + lr;
+      const int q = c * LM_KC + k;  // sample of the frame
+      const float a = span[frame_off + q + 2 * (q / LM_HOP)];
+      const float* brow = buf + k * LM_COLS_LDS + lr;
 #pragma unroll
       for (int t = 0; t < LM_TILES; ++t) acc[t] = mma4(a, brow[16 * t], acc[t]);
     }
@@ -137,7 +150,7 @@ __global__ __launch_bounds__(LM_THREADS) void logmel_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float re = acc[2 * t][r], im = acc[2 * t + 1][r];
-      buf[(16 * wave + 4 * g + r) * PB + 16 * t + lr] = re * re + im * im;
+      buf[(16 * wave + 4 * g + r) * LM_PB_LDS + 16 * t + lr] = re * re + im * im;
     }
   __syncthreads();
 
@@ -145,7 +158,7 @@ __global__ __launch_bounds__(LM_THREADS) void logmel_kernel(
   f32x4_t macc[LM_MELS / 16];
 #pragma unroll
   for (int t = 0; t < LM_MELS / 16; ++t) macc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const float* prow = buf + (16 * wave + lr) * PB;
+  const float* prow = buf + (16 * wave + lr) * LM_PB_LDS;
 #pragma unroll 4
   for (int kk = 0; kk < PB / 4; ++kk) {
     const int k = 4 * kk + g;
