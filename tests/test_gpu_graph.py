@@ -13,7 +13,7 @@ from gpu_common import features_dev, pack, small_cfg, torch_mod
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("dtype,mask", [("bf16", 0), ("fp8", 63)])
+@pytest.mark.parametrize("dtype,mask", [("fp32", 0), ("bf16", 0), ("fp8", 63)])
 def test_graph_replay_matches_eager(dtype, mask):
     from packed_windowed_attention_amd import aut
     torch = torch_mod()

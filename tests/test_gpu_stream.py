@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 ARRIVALS = [150, 420, 800, 1010, 1650, 2400, 2630]
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp8"])
 def test_stream_equals_batch(dtype):
     from packed_windowed_attention_amd import aut
     torch = torch_mod()
