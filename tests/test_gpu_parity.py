@@ -78,6 +78,23 @@ def test_edge_lengths(lens):
     check(y, ref, "fp32", f"lens {list(lens)}")
 
 
+@pytest.mark.parametrize("n_window_infer,dtype", [(100, "bf16"), (400, "fp32"), (900, "bf16")])
+def test_window_sizes(n_window_infer, dtype):
+    """Windows of 13, 52 and 117 tokens (1, 4 and 9 chunks; 117 is the largest
+    that fits the 128-key attention tile), ragged requests with partial last
+    chunks and windows: the whole output against the oracle."""
+    cfg_d = small_cfg(dtype, n_window_infer=n_window_infer)
+    lens = np.array([250, 0, 1737, 37, 901, 2600])
+    feats = si.mel_features(lens, seed=61)
+    P = si.params(cfg_d, seed=61, std=0.05)
+    print(f"case: window of {13 * n_window_infer // 100} tokens, {dtype}", flush=True)
+    y, pl = forward(cfg_d, lens, feats, P)
+    ref, opl = oracle.forward(feats, lens, P, cfg_d)
+    assert pl.copy()[1] == opl["cu_seqlens"]
+    assert max(np.diff(opl["cu_seqlens"])) == 13 * n_window_infer // 100
+    check(y, ref, dtype, f"window {13 * n_window_infer // 100} tokens")
+
+
 def test_empty_batch():
     from packed_windowed_attention_amd import aut
     cfg_d = small_cfg("fp32", encoder_layers=1)
