@@ -95,6 +95,22 @@ def test_window_sizes(n_window_infer, dtype):
     check(y, ref, dtype, f"window {13 * n_window_infer // 100} tokens")
 
 
+@pytest.mark.parametrize("n_window,n_window_infer,dtype", [(25, 400, "fp32"), (60, 960, "bf16"),
+                                                          (10, 160, "bf16")])
+def test_chunk_sizes(n_window, n_window_infer, dtype):
+    """Chunks of 50, 120 and 20 frames (7, 15 and 3 tokens per chunk, windows of
+    8 chunks): other stem geometries and position counts, whole output."""
+    cfg_d = small_cfg(dtype, n_window=n_window, n_window_infer=n_window_infer)
+    lens = np.array([250, 0, 1737, 37, 901])
+    feats = si.mel_features(lens, seed=67)
+    P = si.params(cfg_d, seed=67, std=0.05)
+    print(f"case: chunks of {2 * n_window} frames, {dtype}", flush=True)
+    y, pl = forward(cfg_d, lens, feats, P)
+    ref, opl = oracle.forward(feats, lens, P, cfg_d)
+    assert pl.copy()[1] == opl["cu_seqlens"]
+    check(y, ref, dtype, f"chunks of {2 * n_window} frames")
+
+
 def test_empty_batch():
     from packed_windowed_attention_amd import aut
     cfg_d = small_cfg("fp32", encoder_layers=1)
