@@ -111,6 +111,23 @@ def test_chunk_sizes(n_window, n_window_infer, dtype):
     check(y, ref, dtype, f"chunks of {2 * n_window} frames")
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_odd_widths(dtype):
+    """d_model 192 (3 heads), FFN 200, 24 conv channels, output 72: column
+    tails in every GEMM tile, a k tail in fc2 (K = 200), conv taps of 24
+    channels inside a 64-wide k step; whole output."""
+    cfg_d = small_cfg(dtype, d_model=192, encoder_attention_heads=3, encoder_ffn_dim=200,
+                      downsample_hidden_size=24, output_dim=72)
+    lens = np.array([250, 0, 1737, 37, 901])
+    feats = si.mel_features(lens, seed=71)
+    P = si.params(cfg_d, seed=71, std=0.05)
+    print(f"case: odd widths, {dtype}", flush=True)
+    y, pl = forward(cfg_d, lens, feats, P)
+    ref, opl = oracle.forward(feats, lens, P, cfg_d)
+    assert pl.copy()[1] == opl["cu_seqlens"]
+    check(y, ref, dtype, f"odd widths {dtype}")
+
+
 def test_empty_batch():
     from packed_windowed_attention_amd import aut
     cfg_d = small_cfg("fp32", encoder_layers=1)
