@@ -365,6 +365,33 @@ aut_status aut_mx_matmul(const uint8_t* a_codes, const uint8_t* a_scales, int64_
                          const uint8_t* b_codes, const uint8_t* b_scales, int32_t N, int32_t K,
                          float* out, void* stream);
 
+/* ------------------------------------------------------------------------
+ * One LayerNorm step on its own: the normalisation in front of qkv, fc1 and
+ * the projector (LayerNorm with bias, not RMSNorm: cubic.dev wiki, "Audio
+ * Encoder Component", encoder-layer description), with the kernel the
+ * forward uses.  Per row of d values: y = (x - mean) / sqrt(var + eps) *
+ * gamma + beta, population variance, fp32 statistics (two passes: the mean,
+ * then the mean of squared deviations).
+ *   x:      device fp32 [rows, d], row-major, 16-byte aligned
+ *   gamma,  device fp32 [d] each
+ *   beta:
+ *   dtype:  AUT_FP32: y is fp32 [rows, d];
+ *           AUT_BF16: y is bf16 [rows, d], each value the fp32 result
+ *                     rounded to nearest even;
+ *           AUT_FP8:  y is e4m3 codes [rows, d] and y_scales holds the scale
+ *                     codes (aut_mx_scale_bytes(rows, d) bytes, the MX
+ *                     layout above): each 32-value block of a row quantised
+ *                     from the fp32 results as aut_mx_quantize would; d a
+ *                     multiple of 128.  The scale bytes of the padding rows
+ *                     past `rows` are not written.
+ * d a multiple of 4, at most 2048; y 8-byte aligned.  The caller owns every
+ * buffer.  Returns INVALID_ARG for NULL pointers, misalignment or a
+ * negative count, UNSUPPORTED for a d outside these limits.  Asynchronous on
+ * `stream`. */
+aut_status aut_layernorm(const float* x, int64_t rows, int32_t d, const float* gamma,
+                         const float* beta, float eps, aut_dtype dtype, void* y,
+                         uint8_t* y_scales, void* stream);
+
 /* Kernel classes for the optional per-launch timing below. */
 typedef enum {
   AUT_K_CONV1 = 0,     /* conv1 (+GELU), fp32 vector ALU */

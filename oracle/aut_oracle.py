@@ -326,9 +326,18 @@ _MX_WEIGHTS: dict = {}
 
 def linear_conv_out_mx(u: np.ndarray, w: np.ndarray, b, F: int) -> np.ndarray:
     """conv_out on MX-fp8 operands.  u holds the token features in the
-    channel-major flatten c * F + f; the contraction blocks are 32 consecutive
-    channels of one frequency bin (the GPU stores the stem output bin-major),
-    so both sides are rounded in the order f * C + c and put back."""
+    channel-major flatten c * F + f (the pairing of features and weight
+    columns is unchanged).  Reading: every activation of the conv stem is
+    quantised once, per pixel, in blocks of 32 consecutive channels: that is
+    the only blocking the conv2 and conv3 contractions admit (their 32-value
+    blocks run over channels within one tap, i.e. within one input pixel), and
+    conv_out reads the same kind of tensor, the stem's last activation, so its
+    blocks are those of the same rule: for token j, the 32-channel groups of
+    one frequency bin f.  A dot product does not depend on the order of its
+    terms, so the flatten order fixes which weight meets which feature but not
+    how the contraction is blocked; the weight blocks are the matching sets of
+    columns, {c * F + f : c in one group of 32}.  Both sides are therefore
+    rounded in the order f * C + c and put back."""
     u = np.asarray(u, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
     C = u.shape[1] // F
@@ -338,6 +347,14 @@ def linear_conv_out_mx(u: np.ndarray, w: np.ndarray, b, F: int) -> np.ndarray:
     wq = np.empty_like(w)
     wq[:, perm] = mx_round(w[:, perm])
     return linear(uq, wq, b)
+
+
+def mx_round_pixels(a: np.ndarray) -> np.ndarray:
+    """MX-fp8 round trip of a stem activation [C, H, W]: every pixel's C
+    channel values in blocks of 32 consecutive channels (C a multiple of 32)."""
+    a = np.asarray(a, dtype=np.float64)
+    C = a.shape[0]
+    return mx_round(a.reshape(C, -1).T).T.reshape(a.shape)
 
 
 def _mx_weight(w) -> np.ndarray:
@@ -418,8 +435,9 @@ def frontend(features, feature_lens, P: dict, cfg: dict, chunk_ids=None, fp8: in
     """m-star ``frontend``: chunk, pad, convolve, conv_out, add positions,
     keep the valid tokens.  Returns ([rows, d_model], the plan); ``chunk_ids``
     restricts the work to some chunks (rows returned in chunk order).
-    FP8_CONV: conv2, conv3 and conv_out on MX-fp8 operands (conv_out's blocks
-    are 32 channels of one frequency bin, see ``linear_conv_out_mx``)."""
+    FP8_CONV: conv2, conv3 and conv_out on MX-fp8 operands, each stem
+    activation quantised per pixel in blocks of 32 channels (see
+    ``linear_conv_out_mx``)."""
     pl = plan(feature_lens, cfg)
     d = cfg["d_model"]
     pe = sinusoid_table(cfg["max_source_positions"], d)

@@ -92,6 +92,8 @@ SIGNATURES = {
     "aut_mx_quantize": (c_int, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
     "aut_mx_matmul": (c_int, [c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_int32,
                               c_void_p, c_void_p]),
+    "aut_layernorm": (c_int, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_float, c_int, c_void_p,
+                               c_void_p, c_void_p]),
     "aut_profile_enable": (c_int, [c_int]),
     "aut_profile_collect": (c_int, [POINTER(AutKernelStats)]),
     "aut_last_error": (c_char_p, []),
@@ -255,23 +257,51 @@ def plan_upload(pl: Plan, ws, stream=None):
     _check(lib().aut_plan_upload(pl.handle, _ptr(ws), ws.numel(), _stream_ptr(stream)))
 
 
-def _check_features(features):
-    if features.dtype.is_floating_point is False or str(features.dtype) != "torch.float32":
+def _check_features(features, cfg: AutConfig, n_requests: int):
+    """The kernels read features[b, :, :len_b] for every request b: the
+    tensor must hold that many requests and cfg.num_mel_bins rows each."""
+    if str(features.dtype) != "torch.float32":
         raise TypeError("features must be float32")
     if features.dim() != 3 or not features.is_contiguous():
         raise ValueError("features must be a contiguous [B, mel, T_max] tensor")
+    if features.shape[0] < n_requests:
+        raise ValueError(f"features holds {features.shape[0]} requests, the lengths name {n_requests}")
+    if features.shape[1] != cfg.num_mel_bins:
+        raise ValueError(f"features has {features.shape[1]} mel bins, the configuration {cfg.num_mel_bins}")
+
+
+def _check_f32(t, rows: int, cols: int, what: str, device=None):
+    """A caller-supplied fp32 buffer the kernels write (or read) rows x cols of."""
+    if t is None:
+        raise ValueError(f"{what} is missing")
+    if str(t.dtype) != "torch.float32" or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous float32 tensor")
+    if t.numel() < rows * cols:
+        raise ValueError(f"{what} holds {t.numel()} values, needs {rows} x {cols}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what} is on {t.device}, the features on {device}")
+
+
+def _check_bytes(t, need: int, what: str):
+    if t is None or str(t.dtype) != "torch.uint8" or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous uint8 tensor")
+    if t.numel() < need:
+        raise ValueError(f"{what} holds {t.numel()} bytes, needs {need}")
 
 
 def encode(cfg: AutConfig, features, feature_lens, packed, dtype, out=None, ws=None, stream=None):
     """aut_encode: the whole forward; returns (out [T, output_dim] fp32, plan)."""
     import torch
-    _check_features(features)
+    lens = [int(x) for x in feature_lens]
+    _check_features(features, cfg, len(lens))
     pl = Plan(cfg, feature_lens)
     if out is None:
         out = torch.empty((pl.total_tokens, cfg.output_dim), dtype=torch.float32, device=features.device)
+    _check_f32(out, pl.total_tokens, cfg.output_dim, "out", features.device)
     if ws is None:
         ws = workspace(cfg, pl, dtype, device=features.device)
-    lens = [int(x) for x in feature_lens]
+    _check_bytes(ws, workspace_bytes(cfg, pl, dtype), "ws")
+    _check_bytes(packed, weights_bytes(cfg, dtype), "packed")
     arr = (c_int32 * max(1, len(lens)))(*lens)
     _check(lib().aut_encode(byref(cfg), _ptr(features), features.shape[2], arr, len(lens),
                             _ptr(packed), _dtype(dtype), _ptr(out), _ptr(ws), ws.numel(),
@@ -281,7 +311,10 @@ def encode(cfg: AutConfig, features, feature_lens, packed, dtype, out=None, ws=N
 
 def encode_planned(cfg: AutConfig, pl: Plan, features, packed, dtype, out, ws, stream=None):
     """aut_encode_planned: kernels only, for a plan already uploaded into ws."""
-    _check_features(features)
+    _check_features(features, cfg, pl.B)
+    _check_f32(out, pl.total_tokens, cfg.output_dim, "out", features.device)
+    _check_bytes(ws, workspace_bytes(cfg, pl, dtype), "ws")
+    _check_bytes(packed, weights_bytes(cfg, dtype), "packed")
     _check(lib().aut_encode_planned(byref(cfg), pl.handle, _ptr(features), features.shape[2],
                                     _ptr(packed), _dtype(dtype), _ptr(out), _ptr(ws), ws.numel(),
                                     _stream_ptr(stream)))
@@ -290,7 +323,10 @@ def encode_planned(cfg: AutConfig, pl: Plan, features, packed, dtype, out, ws, s
 
 def frontend(cfg: AutConfig, pl: Plan, features, packed, dtype, hidden, ws, stream=None):
     """aut_frontend: features -> packed hidden [T, d_model] fp32 (plan uploaded)."""
-    _check_features(features)
+    _check_features(features, cfg, pl.B)
+    _check_f32(hidden, pl.total_tokens, cfg.d_model, "hidden", features.device)
+    _check_bytes(ws, workspace_bytes(cfg, pl, dtype), "ws")
+    _check_bytes(packed, weights_bytes(cfg, dtype), "packed")
     _check(lib().aut_frontend(byref(cfg), pl.handle, _ptr(features), features.shape[2],
                               _ptr(packed), _dtype(dtype), _ptr(hidden), _ptr(ws), ws.numel(),
                               _stream_ptr(stream)))
@@ -299,6 +335,10 @@ def frontend(cfg: AutConfig, pl: Plan, features, packed, dtype, hidden, ws, stre
 
 def encode_packed(cfg: AutConfig, pl: Plan, hidden, packed, dtype, out, ws, stream=None):
     """aut_encode_packed: layer stack + projector over packed hidden (plan uploaded)."""
+    _check_f32(hidden, pl.total_tokens, cfg.d_model, "hidden")
+    _check_f32(out, pl.total_tokens, cfg.output_dim, "out", hidden.device)
+    _check_bytes(ws, workspace_bytes(cfg, pl, dtype), "ws")
+    _check_bytes(packed, weights_bytes(cfg, dtype), "packed")
     _check(lib().aut_encode_packed(byref(cfg), pl.handle, _ptr(hidden), _ptr(packed),
                                    _dtype(dtype), _ptr(out), _ptr(ws), ws.numel(),
                                    _stream_ptr(stream)))
@@ -329,6 +369,12 @@ def encode_stream(cfg: AutConfig, features, frames_total: int, windows_final: in
     rows.  Returns the new count of final windows."""
     if str(features.dtype) != "torch.float32" or features.dim() != 2 or not features.is_contiguous():
         raise ValueError("features must be a contiguous float32 [mel, T_max] tensor")
+    if features.shape[0] != cfg.num_mel_bins:
+        raise ValueError(f"features has {features.shape[0]} mel bins, the configuration {cfg.num_mel_bins}")
+    # the request's output rows for the frames received so far
+    rows = Plan(cfg, [int(frames_total)]).total_tokens if int(frames_total) >= 0 else 0
+    _check_f32(out, rows, cfg.output_dim, "out", features.device)
+    _check_bytes(packed, weights_bytes(cfg, dtype), "packed")
     after = c_int32()
     _check(lib().aut_encode_stream(byref(cfg), _ptr(features), features.shape[1], int(frames_total),
                                    int(windows_final), _ptr(packed), _dtype(dtype), _ptr(out),
@@ -437,3 +483,26 @@ def mx_matmul(a_codes, a_scales, b_codes, b_scales, out=None, stream=None):
     _check(lib().aut_mx_matmul(_ptr(a_codes), _ptr(a_scales), M, _ptr(b_codes), _ptr(b_scales), N,
                                K, _ptr(out), _stream_ptr(stream)))
     return out
+
+
+def layernorm(x, gamma, beta, dtype="fp32", eps=1e-5, stream=None):
+    """aut_layernorm: fp32 [R, d] rows on the device -> fp32 / bf16 [R, d],
+    or for "fp8" (e4m3 codes uint8 [R, d], scale codes in the MX layout)."""
+    import torch
+    if str(x.dtype) != "torch.float32" or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D float32 tensor")
+    R, d = x.shape
+    for t in (gamma, beta):
+        if str(t.dtype) != "torch.float32" or t.numel() != d or not t.is_contiguous() or t.device != x.device:
+            raise ValueError("gamma and beta must be contiguous float32 [d] tensors on x's device")
+    dt = _dtype(dtype)
+    scales = None
+    if dt == DTYPES["fp8"]:
+        y = torch.empty((R, d), dtype=torch.uint8, device=x.device)
+        scales = torch.zeros(max(1, mx_scale_bytes(R, d)), dtype=torch.uint8, device=x.device)
+    else:
+        y = torch.empty((R, d), dtype=torch.float32 if dt == DTYPES["fp32"] else torch.bfloat16,
+                        device=x.device)
+    _check(lib().aut_layernorm(_ptr(x), R, d, _ptr(gamma), _ptr(beta), float(eps), dt, _ptr(y),
+                               _ptr(scales) if scales is not None else None, _stream_ptr(stream)))
+    return (y, scales) if scales is not None else y

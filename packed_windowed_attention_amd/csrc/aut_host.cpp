@@ -1240,6 +1240,26 @@ extern "C" aut_status aut_mx_matmul(const uint8_t* a_codes, const uint8_t* a_sca
   return AUT_OK;
 }
 
+extern "C" aut_status aut_layernorm(const float* x, int64_t rows, int32_t d, const float* gamma,
+                                    const float* beta, float eps, aut_dtype dtype, void* y,
+                                    uint8_t* y_scales, void* stream) {
+  if (rows < 0) return fail(AUT_ERR_INVALID_ARG, "rows = %lld is negative", (long long)rows);
+  if (dtype != AUT_FP32 && dtype != AUT_BF16 && dtype != AUT_FP8)
+    return fail(AUT_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (d <= 0 || d % 4 || d > 2048 || (dtype == AUT_FP8 && d % 128))
+    return fail(AUT_ERR_UNSUPPORTED, "d = %d: need a multiple of 4 (of 128 for fp8), at most 2048", d);
+  if (rows >= ((int64_t)1 << 31)) return fail(AUT_ERR_UNSUPPORTED, "rows = %lld: at most 2^31 - 1", (long long)rows);
+  if (rows == 0) return AUT_OK;
+  if (!x || !gamma || !beta || !y || (dtype == AUT_FP8 && !y_scales))
+    return fail(AUT_ERR_INVALID_ARG, "NULL pointer");
+  if (((size_t)x & 15) || ((size_t)y & 7) || ((size_t)gamma & 15) || ((size_t)beta & 15))
+    return fail(AUT_ERR_INVALID_ARG, "x, gamma and beta must be 16-byte aligned, y 8-byte aligned");
+  hipError_t e = aut::launch_layernorm(x, gamma, beta, y, (int)rows, d, eps, dtype, (hipStream_t)stream,
+                                       y_scales);
+  if (e != hipSuccess) return fail(AUT_ERR_HIP, "layernorm launch failed: %s", hipGetErrorString(e));
+  return AUT_OK;
+}
+
 // ---------------------------------------------------------------------------
 // timing and errors
 // ---------------------------------------------------------------------------

@@ -1069,6 +1069,8 @@ hipError_t launch_gemm_f8(const GemmArgs& a, int amode, int epi, hipStream_t s) 
 hipError_t launch_gemm256(const GemmArgs& a, int amode, int epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (!epilogue_fits(a, epi)) return hipErrorInvalidValue;
+  // gathered A: one descriptor over the whole buffer, 32-bit offsets below OOB
+  if (amode != A_PLAIN && a.a_bytes >= (size_t)OOB) return hipErrorInvalidValue;
   const int bn = g_gemm256_force_bn ? g_gemm256_force_bn : pick_bn(a.M, a.N);
   switch (bn) {
     case 320: return dispatch<320>(a, amode, epi, s);

@@ -100,8 +100,10 @@ def workload(name):
     return si.workload(name)
 
 
-def sample_windows(pl_oracle: dict, seed: int, n_random: int = 2):
-    """First, last, shortest, longest partial and a few random windows."""
+def sample_windows(pl_oracle: dict, seed: int, n_random: int = 4, at_least: int = 8):
+    """First, last, shortest, longest partial and n_random random windows,
+    topped up with further random ones until at least ``at_least`` distinct
+    windows (or all of them) are picked."""
     wl = pl_oracle["window_lengths"]
     nw = len(wl)
     pick = {0, nw - 1, int(np.argmin(wl))}
@@ -109,5 +111,10 @@ def sample_windows(pl_oracle: dict, seed: int, n_random: int = 2):
     if partial:
         pick.add(max(partial, key=lambda w: (wl[w], -w)))
     rng = np.random.default_rng(seed)
-    pick.update(int(x) for x in rng.choice(nw, size=min(n_random, nw), replace=False))
+    order = [int(x) for x in rng.permutation(nw)]
+    pick.update(order[:min(n_random, nw)])
+    for w in order[min(n_random, nw):]:
+        if len(pick) >= min(at_least, nw):
+            break
+        pick.add(w)
     return sorted(pick)

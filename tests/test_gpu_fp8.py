@@ -36,8 +36,12 @@ MX_MATMUL_TOL = 5e-5
 FP8_NOISE_FACTOR = 2.0
 FP8_BF16_SLACK = 2e-5
 # the pages' criterion for an 8-bit variant: cosine similarity to the
-# full-precision encoder > 0.999, read as the mean over tokens
+# full-precision encoder > 0.999, for every token
 PAGE_COS = 0.999
+# the product classes on MX-fp8 that meet it at 24 layers, d 1280: the conv
+# stem alone.  Each layer product on e4m3 costs about 7e-4 of cosine and the
+# projector about 1.5e-3, so any of them breaks the bar on some token.
+PAGE_MASK = 32
 
 
 def mx_inputs(R, K, seed):
@@ -162,20 +166,23 @@ def test_rag_fp8():
     check_fp8(y, ref_q, ref, "rag fp8")
 
 
-@pytest.mark.parametrize("mask", [63, 33])
+@pytest.mark.parametrize("mask", [PAGE_MASK, 63, 1])
 def test_wide_fp8_sampled_windows(mask):
-    """Full-width workload (24 layers, d 1280) under AUT_FP8, sampled windows.
-    mask 33 (the conv stem and the q/k/v projection) meets the pages' cosine
-    > 0.999 (mean over tokens) against the unquantized encoder; every product
-    on MX-fp8 does not (e4m3 keeps 3 mantissa bits: about 7e-4 of cosine per
-    layer product) and is reported."""
+    """Full-width workload (24 layers, d 1280) under AUT_FP8, at least 8
+    sampled windows (first, last, shortest, the longest partial one, random
+    ones).  Every mask: the GPU within the quantisation noise bound of the
+    oracle with the same products quantised.  The conv stem on MX-fp8
+    (PAGE_MASK) meets the pages' per-token cosine > 0.999 against the
+    unquantised encoder on every token; every product on MX-fp8 (63, the
+    fastest) and q/k/v alone (1) do not, and their cosines are reported."""
     cfg_d, lens, feats, P = workload("wide")
     cfg_d = dict(cfg_d, dtype="fp8", fp8_gemms=mask)
     print(f"case: wide fp8 mask {mask}, sampled windows", flush=True)
     y, pl = forward(cfg_d, lens, feats, P)
     opl = oracle.plan(lens, cfg_d)
     assert pl.copy()[1] == opl["cu_seqlens"]
-    wins = sample_windows(opl, seed=si.workload_seed("wide") + 3, n_random=1)
+    wins = sample_windows(opl, seed=si.workload_seed("wide") + 3)
+    assert len(wins) >= 8, wins
     res_q = oracle.forward_windows(feats, lens, P, cfg_d, wins, fp8=mask)
     res = oracle.forward_windows(feats, lens, P, cfg_d, wins)
     cos = []
@@ -184,6 +191,7 @@ def test_wide_fp8_sampled_windows(mask):
         g = y[r0:r0 + ref_q.shape[0]]
         cos.append(check_fp8(g, ref_q, res[w][1], f"wide mask {mask} window {w}"))
     cos = np.concatenate(cos)
-    print(f"[wide mask {mask}] vs unquantized: mean cos {cos.mean():.6f} min {cos.min():.6f}", flush=True)
-    if mask == 33:
-        assert cos.mean() > PAGE_COS
+    print(f"[wide mask {mask}] vs unquantized over windows {wins}: min cos {cos.min():.6f} "
+          f"mean {cos.mean():.6f}", flush=True)
+    if mask == PAGE_MASK:
+        assert cos.min() > PAGE_COS

@@ -167,7 +167,9 @@ def test_rag_bf16():
     print("case: rag bf16", flush=True)
     y, pl = forward(cfg_d, lens, feats, P)
     ref, opl = oracle.forward(feats, lens, P, cfg_d)
-    assert pl.copy()[1] == opl["cu_seqlens"]
+    # the printed cu_seqlens of 3.0, 8.0, 17.37 and 30.0 s (tokens 39, 104,
+    # 226, 390; windows of 104 tokens per request, then the remainder)
+    assert pl.copy()[1] == opl["cu_seqlens"] == [0, 39, 143, 247, 351, 369, 473, 577, 681, 759]
     check(y, ref, "bf16", "rag")
 
 
@@ -180,7 +182,9 @@ def test_large_sampled_windows(name):
     opl = oracle.plan(lens, cfg_d)
     assert pl.copy()[1] == opl["cu_seqlens"]
     assert np.isfinite(y).all()
-    wins = sample_windows(opl, seed=si.workload_seed(name), n_random=1)
+    wins = sample_windows(opl, seed=si.workload_seed(name))
+    assert len(wins) >= 8, wins
+    print(f"[{name}] windows {wins}", flush=True)
     res = oracle.forward_windows(feats, lens, P, cfg_d, wins)
     for w, (r0, ref) in res.items():
         check(y[r0:r0 + ref.shape[0]], ref, "bf16", f"{name} window {w} (rows {r0}+{ref.shape[0]})")
@@ -241,7 +245,8 @@ def test_wide_bench_launch_config():
     opl = oracle.plan(lens, cfg_d)
     assert pl.copy()[1] == opl["cu_seqlens"]
     assert np.isfinite(y).all()
-    wins = sample_windows(opl, seed=si.workload_seed("wide") + 7, n_random=2)
+    wins = sample_windows(opl, seed=si.workload_seed("wide") + 7)
+    assert len(wins) >= 8, wins
     res = oracle.forward_windows(feats, lens, P, cfg_d, wins)
     for w, (r0, ref) in res.items():
         check(y[r0:r0 + ref.shape[0]], ref, "bf16", f"wide/bench window {w} (rows {r0}+{ref.shape[0]})")

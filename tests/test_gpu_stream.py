@@ -2,18 +2,38 @@
 audio arrives in pieces, re-encoded from its first non-final window at each
 step, ends bit-identical to the batch encode, and rows that are final are
 never rewritten (windows are independent: m-star module summary; openarchlab
-"1A", section 4)."""
+"1A", section 4).  At every arrival the rows written so far are also checked
+against the float64 oracle's forward of the request as it stands (its first
+n frames), and the final output against the oracle's forward of the whole
+request, at the mode's tolerance (fp32: relative 1e-4; bf16: max-abs 2e-2 and
+per-token cosine 0.999; MX-fp8: within the quantisation noise bound of the
+oracle with the same products quantised)."""
 from __future__ import annotations
 
 import numpy as np
 import pytest
 
+import oracle
 import synth_inputs as si
-from gpu_common import forward, pack, small_cfg, torch_mod
+from gpu_common import check, forward, pack, small_cfg, torch_mod
+from test_gpu_fp8 import check_fp8
 
 pytestmark = pytest.mark.gpu
 
 ARRIVALS = [150, 420, 800, 1010, 1650, 2400, 2630]
+FP8_MASK = 63
+
+
+def check_vs_oracle(g, feats, n, P, cfg_d, dtype, what):
+    """Rows g against the oracle's forward of the request's first n frames."""
+    f = np.ascontiguousarray(feats[:, :, :n])
+    ref, _ = oracle.forward(f, np.array([n]), P, cfg_d)
+    ref = ref[:g.shape[0]]
+    if dtype == "fp8":
+        ref_q, _ = oracle.forward(f, np.array([n]), P, cfg_d, fp8=FP8_MASK)
+        check_fp8(g, ref_q[:g.shape[0]], ref, what)
+    else:
+        check(g, ref, dtype, what)
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp8"])
@@ -21,6 +41,8 @@ def test_stream_equals_batch(dtype):
     from packed_windowed_attention_amd import aut
     torch = torch_mod()
     cfg_d = small_cfg(dtype)
+    if dtype == "fp8":
+        cfg_d["fp8_gemms"] = FP8_MASK
     L = ARRIVALS[-1]
     lens = np.array([L])
     feats = si.mel_features(lens, seed=31)
@@ -50,9 +72,13 @@ def test_stream_equals_batch(dtype):
         # rows final now equal the batch result bit for bit
         rf = sp["row_begin"] + 104 * (wf_new - wf)
         np.testing.assert_array_equal(o[:rf], y_batch[:rf])
+        # every row written so far against the oracle on the frames received
+        check_vs_oracle(o[:r1].astype(np.float64), feats, n, P, cfg_d, dtype, f"stream {dtype} at {n} frames")
         wf = wf_new
         prev = o
-    np.testing.assert_array_equal(out.cpu().numpy(), y_batch)
+    final = out.cpu().numpy()
+    np.testing.assert_array_equal(final, y_batch)
+    check_vs_oracle(final.astype(np.float64), feats, L, P, cfg_d, dtype, f"stream {dtype} final")
 
 
 def test_stream_argument_checks():

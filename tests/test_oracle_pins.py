@@ -795,6 +795,36 @@ def test_conv_out_mx_vs_reorder():
     assert check_conv_out_mx() < 1e-12
 
 
+def test_stem_mx_is_one_per_pixel_quantisation():
+    """The three MX-fp8 stem products see the same rounding of an activation:
+    conv2 / conv3 on MX operands equal the exact convolution of the input
+    rounded per pixel (blocks of 32 channels) with the weights rounded per tap
+    over input channels; conv_out on MX operands equals the exact product of
+    the per-pixel-rounded stem output, flattened c * 16 + f, with the weight
+    rounded over each bin's 32-channel groups."""
+    r = np.random.default_rng(21)
+    C, F, T = 64, 16, 5
+    x = r.standard_normal((C, 9, 8)) * np.exp2(r.integers(-8, 8, (C, 1, 1)))
+    w = r.standard_normal((7, C, 3, 3)) * 0.05
+    b = r.standard_normal(7)
+    wq = np.zeros_like(w)
+    for kh in range(3):
+        for kw in range(3):
+            wq[:, :, kh, kw] = torch_mx_round(w[:, :, kh, kw])
+    ref = ao.conv2d_k3s2p1(ao.mx_round_pixels(x), wq, b)
+    assert np.abs(ao.conv2d_k3s2p1_mx(x, w, b) - ref).max() < 1e-12
+    a3 = r.standard_normal((C, F, T)) * np.exp2(r.integers(-8, 8, (C, 1, 1)))
+    wo = r.standard_normal((9, C * F)) * 0.05
+    u = ao.flatten_tokens(a3, T)
+    uq = ao.flatten_tokens(ao.mx_round_pixels(a3), T)
+    woq = np.zeros_like(wo)
+    for f in range(F):
+        cols = np.arange(C) * F + f
+        woq[:, cols] = torch_mx_round(wo[:, cols])
+    ref = uq @ woq.T
+    assert np.abs(ao.linear_conv_out_mx(u, wo, None, F) - ref).max() < 1e-12
+
+
 def test_fp8_encoder_masks():
     cfg = small_cfg(encoder_layers=1, downsample_hidden_size=32)
     lens = np.array([420], dtype=np.int32)

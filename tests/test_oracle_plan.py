@@ -101,6 +101,12 @@ def test_known_workload_sizes():
         wl += [104] * (t // 104) + ([t % 104] if t % 104 else [])
     assert pl["window_lengths"] == wl
     assert pl["cu_seqlens"] == list(np.cumsum([0] + wl))
+    # the same values as literals, worked out by hand: 300 frames -> 39
+    # tokens, 800 -> 104, 1737 -> 13 * 17 + ceil(37 / 8) = 226, 3000 -> 390;
+    # windows 39 | 104 | 104, 104, 18 | 104, 104, 104, 78
+    assert pl["tokens_per_request"] == [39, 104, 226, 390]
+    assert pl["window_lengths"] == [39, 104, 104, 104, 18, 104, 104, 104, 78]
+    assert pl["cu_seqlens"] == [0, 39, 143, 247, 351, 369, 473, 577, 681, 759]
 
 
 def test_empty_requests_and_edges():
