@@ -44,7 +44,6 @@ constexpr int KU = 8;       // 16-byte units per row per k step
 constexpr int BK = 64;      // bf16 per row per k step
 constexpr int GROUP_M = 8;
 constexpr unsigned OOB = 0x80000000u;  // an offset past every buffer here: loads zero
-int g_gemm_2w = 0;  // 256 x 160 tiles on the two-workgroup kernel
 
 // Record count of a tile's A descriptor (based at the tile's first row): the
 // rest of the matrix, capped at 2^31 bytes.  A tile reads at most BM rows past
@@ -502,10 +501,10 @@ void gemm256_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
 // Eight-wave variant for wide column tiles (BN = 256 or 320): 8 waves (2 per
 // SIMD) in a 2 x 4 grid, each wave 128 x BN/4 (128 or 160 accumulators), two
 // LDS stages of 64 or 72 KiB.  Fewer operand bytes per flop than the
-// four-wave kernel: the memory path, not the matrix cores, bounds these GEMMs
-// (about one 128-byte request per 10 cycles per CU at ~420 cycles of L2
-// latency), and a 256 x 320 tile needs 7.0 bytes per k step per 1000 flops
-// against 10.2 for 256 x 160.
+// four-wave kernel (a 256 x 320 tile needs 7.0 bytes per k step per 1000
+// flops against 10.2 for 256 x 160).  With both waves of a SIMD reading,
+// loading and multiplying in step, the matrix cores were busy about half the
+// cycles; the ping-pong schedule below offsets the two rows of waves.
 template <int BN, int AMODE, int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
@@ -608,58 +607,100 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   const int nk = (K + BK - 1) / BK;
   const int lrow = lane & 15;
   const int g = lane >> 4;
-  // one step from a stage: wait for this thread's loads of step kt (nothing
-  // later is in flight yet), barrier so that every wave's loads have landed
-  // and step kt - 1 is consumed, then the matrix instructions of the two
-  // 32-deep halves of the step.  The loads of step kt + 1 into the other stage
-  // go out after the first fragment reads, so that their issue overlaps the
-  // reads' latency; they are unconditional (past the last step every offset
-  // is out of range and they write zeros, waited for before the epilogue) so
-  // that the step stays one block for the scheduler.
-  auto step = [&](int kt, const u32x4_t* As_s, const u32x4_t* Bs_s, u32x4_t* As_n, u32x4_t* Bs_n)
-      __attribute__((always_inline)) {
-    wait_vmcnt<0>();
+  // Ping-pong schedule.  The two rows of waves, G0 (wm = 0) and G1 (wm = 1),
+  // one wave of each per SIMD, run one phase apart.  A phase is either the
+  // 40 matrix instructions of one 32-deep half step or the fragment reads of
+  // the next half step (plus this wave's share of a step's loads), and every
+  // phase ends at a barrier.  So while one group's waves issue matrix
+  // instructions, at raised priority, the other group's read LDS and issue
+  // the loads: a SIMD's two waves no longer compete for the same issue slots
+  // at the same moments.  Stage kt % 2 serves step kt; the loads of step
+  // kt + 1 fill the other stage, G1's share in phase 0 of step kt and G0's in
+  // phase 3 of step kt - 1, after every wave has finished reading step kt - 1
+  // there (the readers wait for their reads before the barrier that precedes
+  // a refill).  Each output still sums its k steps in increasing order.
+  FragBF16 xa[8], wb[NTW];
+  auto rd = [&](const u32x4_t* As_s, const u32x4_t* Bs_s, int h) __attribute__((always_inline)) {
+    const int u = 4 * h + g;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int r = wn * WN + 16 * j + lrow;
+      frag_from_units(wb[j], Bs_s[r * KU + swz(u, r)], zero_unit());
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = wm * 128 + 16 * i + lrow;
+      frag_from_units(xa[i], As_s[r * KU + swz(u, r)], zero_unit());
+    }
+  };
+  auto mm = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) mma16_k32(acc[j][i], wb[j], xa[i]);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto bar = [&]() __attribute__((always_inline)) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int u = 4 * h + g;
-      FragBF16 xa[8], wb[NTW];
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        const int r = wn * WN + 16 * j + lrow;
-        frag_from_units(wb[j], Bs_s[r * KU + swz(u, r)], zero_unit());
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = wm * 128 + 16 * i + lrow;
-        frag_from_units(xa[i], As_s[r * KU + swz(u, r)], zero_unit());
-      }
-      if (h == 0) issue(kt + 1, As_n, Bs_n);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) mma16_k32(acc[j][i], wb[j], xa[i]);
-      __builtin_amdgcn_sched_group_barrier(0x100, NTW + 2, 0);  // DS reads
-      if (h == 0) __builtin_amdgcn_sched_group_barrier(0x020, A_LOADS + B_LOADS, 0);  // loads
-#pragma unroll
-      for (int i = 0; i < 6; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, NTW, 0);     // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // DS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTW, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  };
+  // s_waitcnt lgkmcnt(0) alone: this wave's fragment reads have returned
+  auto lgkm0 = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
   };
 
   issue(0, As0, Bs0);
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, As0, Bs0, As1, Bs1);
-    if (kt + 1 < nk) step(kt + 1, As1, Bs1, As0, Bs0);
+  wait_vmcnt<0>();
+  bar();
+  // Both groups pass the same number of barriers: 1 + 4 per step.
+  if (wm == 0) {
+    rd(As0, Bs0, 0);                          // phase -1: read (0, h0), G0's loads of step 1
+    if (1 < nk) issue(1, As1, Bs1);
+    lgkm0();
+    bar();
+    auto g0step = [&](int kt, const u32x4_t* As_s, const u32x4_t* Bs_s, u32x4_t* As_n, u32x4_t* Bs_n)
+        __attribute__((always_inline)) {
+      mm();                                   // phase 0: (kt, h0)
+      bar();
+      rd(As_s, Bs_s, 1);                      // phase 1: read (kt, h1)
+      lgkm0();
+      bar();
+      mm();                                   // phase 2: (kt, h1)
+      wait_vmcnt<0>();                        // this wave's loads of step kt + 1
+      bar();
+      if (kt + 1 < nk) rd(As_n, Bs_n, 0);     // phase 3: read (kt + 1, h0), G0's loads of kt + 2
+      if (kt + 2 < nk) issue(kt + 2, (u32x4_t*)As_s, (u32x4_t*)Bs_s);
+      lgkm0();
+      bar();
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      g0step(kt, As0, Bs0, As1, Bs1);
+      if (kt + 1 < nk) g0step(kt + 1, As1, Bs1, As0, Bs0);
+    }
+  } else {
+    bar();                                    // phase -1
+    auto g1step = [&](int kt, const u32x4_t* As_s, const u32x4_t* Bs_s, u32x4_t* As_n, u32x4_t* Bs_n)
+        __attribute__((always_inline)) {
+      rd(As_s, Bs_s, 0);                      // phase 0: read (kt, h0), G1's loads of kt + 1
+      if (kt + 1 < nk) issue(kt + 1, As_n, Bs_n);
+      lgkm0();
+      bar();
+      mm();                                   // phase 1: (kt, h0)
+      bar();
+      rd(As_s, Bs_s, 1);                      // phase 2: read (kt, h1)
+      lgkm0();
+      wait_vmcnt<0>();                        // this wave's loads of step kt + 1
+      bar();
+      mm();                                   // phase 3: (kt, h1)
+      bar();
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      g1step(kt, As0, Bs0, As1, Bs1);
+      if (kt + 1 < nk) g1step(kt + 1, As1, Bs1, As0, Bs0);
+    }
   }
-  wait_vmcnt<0>();  // the zero-filling loads of the step past the last
-
   staged_epilogue<BN, WN, NT8, EPI>(p, m0, n0, wm, wn, tid, acc, As0, As1, Bs0, Bs1);
 }
 
@@ -905,250 +946,6 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   staged_epilogue<BN, WN, NT8, EPI>(p, m0, n0, wm, wn, tid, acc, As0, As1, Bs0, Bs1);
 }
 
-// Two-workgroup variant: 4 waves (one per SIMD) in a 2 x 2 grid, each wave
-// 128 x BN/2, and three LDS stages of k = 32 (64 bytes per tile row: 26 KiB
-// for BN = 160), 78 KiB per workgroup, so that two workgroups share a CU.
-// Each SIMD then runs one wave of each, and the two workgroups keep their own
-// barriers: while one waits at a barrier, on its first fragment reads after
-// it, or runs its epilogue, the other's matrix instructions keep the matrix
-// core busy.  Loads run two steps ahead (three stages), so a step's barrier
-// also frees the stage the loads of step + 2 fill.
-//
-// LDS rows are 64 bytes, four 16-byte units; unit u of row r is stored at
-// u ^ f(r), f(r) = ((r >> 1) ^ (r >> 2)) & 3: the 8 rows of a fragment read's
-// 8-lane cycle, and the 16 rows of a 16-lane one, fall on distinct banks.
-//
-// The epilogue writes from the accumulators: 4 consecutive columns of a row
-// per lane and instruction (8 bytes bf16, 16 bytes fp32), the column tiles of
-// a row block back to back so that a row's bytes reach L2 together.
-__device__ __forceinline__ int swz4(int unit, int row) { return unit ^ (((row >> 1) ^ (row >> 2)) & 3); }
-
-template <int BN, int AMODE, int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm2w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
-  constexpr int NT4 = 256;
-  constexpr int BK2 = 32;                    // bf16 per row per k step
-  constexpr int KU2 = 4;                     // 16-byte units per row per k step
-  constexpr int WN = BN / 2;                 // columns per wave
-  constexpr int NTW = WN / 16;               // 16-column tiles per wave
-  constexpr int A_UNITS = BM * KU2;          // 1024 units per stage
-  constexpr int B_UNITS = BN * KU2;
-  constexpr int A_WL = A_UNITS / 64;         // 16 wave-loads of 64 units
-  constexpr int B_WL = B_UNITS / 64;         // 10 for BN = 160
-  constexpr int A_LOADS = A_WL / 4;          // per wave
-  constexpr int B_LOADS_MAX = (B_WL + 3) / 4;
-  static_assert(B_UNITS % 64 == 0 && A_WL % 4 == 0, "whole wave-loads");
-  static_assert(EPI != EPI_GELU_MX, "bf16 epilogues only");
-  __shared__ u32x4_t As0[A_UNITS], As1[A_UNITS], As2[A_UNITS];
-  __shared__ u32x4_t Bs0[B_UNITS], Bs1[B_UNITS], Bs2[B_UNITS];
-
-  const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (tile >= nM * nN) return;
-  const int per_group = GROUP_M * nN;
-  const int group = tile / per_group;
-  const int first_m = group * GROUP_M;
-  const int gsize = min(nM - first_m, GROUP_M);
-  const int in_g = tile - group * per_group;
-  const int m0 = (first_m + in_g % gsize) * BM;
-  const int n0 = (in_g / gsize) * BN;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..3
-  const int wm = wave >> 1, wn = wave & 1;
-  const int M = p.M, N = p.N, K = p.K;
-
-  // wave-load q fills LDS units [64 q, 64 q + 64): rows 16 q + l / 4, physical
-  // unit l % 4, i.e. logical unit (l % 4) ^ f(l / 4) for lane l (f depends on
-  // row bits 1..3 only, the same for every q)
-  const int lrow4 = lane >> 2;
-  const int lunit = (lane & 3) ^ (((lrow4 >> 1) ^ (lrow4 >> 2)) & 3);
-  const char* a_base;
-  unsigned a_bytes;
-  if (AMODE == A_PLAIN) {
-    a_base = (const char*)p.A + (size_t)m0 * p.lda * 2;
-    a_bytes = tile_records((size_t)(M - m0) * p.lda * 2);
-  } else {
-    a_base = (const char*)p.A;
-    a_bytes = (unsigned)p.a_bytes;
-  }
-  // A wave-loads of this wave: q = 4 j + wave, rows 16 q + lrow4
-  const unsigned a_step = (unsigned)(64 * p.lda * 2);
-  const unsigned a_off0 = (unsigned)((16 * wave + lrow4) * p.lda * 2);
-  unsigned a_rowoff[A_LOADS];
-  ConvGather<A_LOADS, 2> cg;  // (full size in every mode: see ConvGather)
-  if (AMODE != A_PLAIN) {
-#pragma unroll
-    for (int j = 0; j < A_LOADS; ++j) {
-      const int m = m0 + 16 * (4 * j + wave) + lrow4;
-      if (AMODE == A_ROWMAP) {
-        a_rowoff[j] = m < M ? (unsigned)((size_t)(p.rowmap[m] - p.rowmap_base) * p.lda * 2) : OOB;
-      } else {
-        cg.row(p, j, m);
-      }
-    }
-    if (AMODE == A_CONV) cg.start(lunit * 8, p.cin);
-  }
-  // B wave-loads of this wave: q = 4 j + wave < B_WL
-  const int b_loads = (B_WL - wave + 3) / 4;   // wave-uniform: 3, 3, 2, 2 for B_WL = 10
-  const char* b_base = (const char*)p.B + (size_t)n0 * p.ldb * 2;
-  const unsigned b_bytes = (unsigned)((size_t)(N - n0) * p.ldb * 2);
-  const unsigned b_step = (unsigned)(64 * p.ldb * 2);
-  const unsigned b_off0 = (unsigned)((16 * wave + lrow4) * p.ldb * 2);
-  const __amdgpu_buffer_rsrc_t a_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)a_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t b_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_bytes, 0x00020000);
-
-  auto issue = [&](int kt, u32x4_t* As_s, u32x4_t* Bs_s) __attribute__((always_inline)) {
-    const int k = kt * BK2 + lunit * 8;
-    const unsigned koff = k < K ? (unsigned)(2 * k) : OOB;
-    if (AMODE == A_CONV) {
-      const int toff = cg.tap_offset(p);
-#pragma unroll
-      for (int j = 0; j < A_LOADS; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(4 * j + wave) * 64]), 16,
-                                                 cg.offset(j, toff), 0, 0, 0);
-      cg.advance(BK2, p.cin);  // steps are issued in increasing order
-    } else {
-#pragma unroll
-      for (int j = 0; j < A_LOADS; ++j) {
-        const unsigned off = AMODE == A_PLAIN ? a_off0 + j * a_step + koff
-                                              : (a_rowoff[j] == OOB ? OOB : a_rowoff[j] + koff);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(4 * j + wave) * 64]), 16,
-                                                 off, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < B_LOADS_MAX; ++j) {
-      if (j < b_loads)  // uniform per wave
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dma_dst(&Bs_s[(4 * j + wave) * 64]), 16,
-                                                 b_off0 + j * b_step + koff, 0, 0, 0);
-    }
-  };
-
-  f32x4_t acc[NTW][8];
-#pragma unroll
-  for (int j = 0; j < NTW; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = (K + BK2 - 1) / BK2;
-  const int lrow = lane & 15;
-  const int g = lane >> 4;
-  // step kt from stage kt % 3: this thread's loads of step kt have landed
-  // when at most those of step kt + 1 are still in flight; the barrier then
-  // makes every wave's loads visible and retires step kt - 1, whose stage
-  // the loads of step kt + 2 refill.
-  auto step = [&](int kt, const u32x4_t* As_s, const u32x4_t* Bs_s, u32x4_t* As_n, u32x4_t* Bs_n)
-      __attribute__((always_inline)) {
-    if (kt + 1 < nk) {
-      if (b_loads == B_LOADS_MAX) wait_vmcnt<A_LOADS + B_LOADS_MAX>();
-      else wait_vmcnt<A_LOADS + B_WL / 4>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    FragBF16 xa[8], wb[NTW];
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int r = wn * WN + 16 * j + lrow;
-      frag_from_units(wb[j], Bs_s[r * KU2 + swz4(g, r)], zero_unit());
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = wm * 128 + 16 * i + lrow;
-      frag_from_units(xa[i], As_s[r * KU2 + swz4(g, r)], zero_unit());
-    }
-    if (kt + 2 < nk) issue(kt + 2, As_n, Bs_n);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) mma16_k32(acc[j][i], wb[j], xa[i]);
-    __builtin_amdgcn_sched_group_barrier(0x100, NTW + 2, 0);                    // DS reads
-    __builtin_amdgcn_sched_group_barrier(0x020, A_LOADS + B_LOADS_MAX, 0);      // loads
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, NTW, 0);     // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // DS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTW, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  issue(0, As0, Bs0);
-  if (1 < nk) issue(1, As1, Bs1);
-  for (int kt = 0; kt < nk; kt += 3) {
-    step(kt, As0, Bs0, As2, Bs2);
-    if (kt + 1 < nk) step(kt + 1, As1, Bs1, As0, Bs0);
-    if (kt + 2 < nk) step(kt + 2, As2, Bs2, As1, Bs1);
-  }
-
-  // ---- epilogue from the accumulators ------------------------------------
-  constexpr bool F32 = EPI == EPI_RESID || EPI == EPI_PE || EPI == EPI_STORE_F32;
-  float4 bq[NTW];
-#pragma unroll
-  for (int j = 0; j < NTW; ++j) {
-    const int n = n0 + wn * WN + 16 * j + 4 * g;
-    bq[j] = (p.bias && n < N) ? *reinterpret_cast<const float4*>(p.bias + n)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = m0 + wm * 128 + 16 * i + lrow;
-    if (m >= M) break;  // rows only grow with i
-    if constexpr (F32) {
-      // the row's additions first, then its stores (a load issued after a
-      // store waits for it)
-      float4 add[NTW];
-      const float* src = nullptr;
-      if (EPI == EPI_RESID) src = (const float*)p.out + (size_t)m * p.ldo;
-      if (EPI == EPI_PE) src = p.pe + (size_t)(p.rowmap[m] % p.tpc) * N;
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        const int n = n0 + wn * WN + 16 * j + 4 * g;
-        add[j] = (src && n < N) ? *reinterpret_cast<const float4*>(src + n) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        const int n = n0 + wn * WN + 16 * j + 4 * g;
-        if (n >= N) continue;
-        const f32x4_t a = acc[j][i];
-        *reinterpret_cast<float4*>((float*)p.out + (size_t)m * p.ldo + n) =
-            make_float4(a[0] + bq[j].x + add[j].x, a[1] + bq[j].y + add[j].y,
-                        a[2] + bq[j].z + add[j].z, a[3] + bq[j].w + add[j].w);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        const int n = n0 + wn * WN + 16 * j + 4 * g;
-        if (n >= N) continue;
-        const f32x4_t a = acc[j][i];
-        float v[4] = {a[0] + bq[j].x, a[1] + bq[j].y, a[2] + bq[j].z, a[3] + bq[j].w};
-        if (EPI == EPI_STORE_GELU) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = gelu_bf16(v[r]);
-        }
-        *reinterpret_cast<u32x2_t*>((bf16_t*)p.out + (size_t)m * p.ldo + n) =
-            u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      }
-    }
-  }
-}
-
-template <int BN, int AMODE, int EPI>
-hipError_t run2w(const GemmArgs& a, hipStream_t s) {
-  const int nM = (a.M + BM - 1) / BM;
-  const int nN = (a.N + BN - 1) / BN;
-  const int tiles = nM * nN;
-  const int per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL((gemm2w_kernel<BN, AMODE, EPI>), dim3(8 * per_xcd), dim3(256), 0, s, a, nM, nN,
-                     per_xcd);
-  return hipGetLastError();
-}
-
 template <int BN, int AMODE, int EPI>
 hipError_t run8_f8(const GemmArgs& a, hipStream_t s) {
   const int nM = (a.M + BM - 1) / BM;
@@ -1187,10 +984,7 @@ hipError_t run(const GemmArgs& a, hipStream_t s) {
 template <int BN, int AMODE, int EPI>
 hipError_t run_any(const GemmArgs& a, hipStream_t s) {
   if constexpr (BN >= 256) return run8<BN, AMODE, EPI>(a, s);
-  else if constexpr (BN == 160 && EPI != EPI_GELU_MX) {
-    if (g_gemm_2w) return run2w<BN, AMODE, EPI>(a, s);
-    return run<BN, AMODE, EPI>(a, s);
-  } else return run<BN, AMODE, EPI>(a, s);
+  else return run<BN, AMODE, EPI>(a, s);
 }
 
 template <int BN>
