@@ -213,6 +213,25 @@ aut_status aut_encode(const aut_config* cfg, const float* features, int32_t T_ma
                       const int32_t* feature_lens, int32_t B, const void* packed, aut_dtype dtype,
                       float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* aut_encode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same plan and kernels, with the workspace in a library-owned device
+ * scratch array of 256 MiB per GPU (allocated with the library's code object
+ * when it is loaded on that GPU, held until the process ends) instead of a
+ * caller buffer.  Neither it nor anything it calls allocates device or pinned
+ * memory; the plan tables are copied from the plan's host memory directly
+ * (pageable), so the call may wait for the stream's earlier work.
+ * Returns AUT_ERR_WORKSPACE_TOO_SMALL, before touching the GPU, for a batch
+ * whose aut_workspace_bytes exceeds 256 MiB (e.g. d_model 1280 with C 480
+ * fits about 300 s of audio per call at conv_chunksize 16).  All calls on one
+ * GPU share its scratch: calls that overlap in time on one GPU (other streams
+ * or threads) race and must be serialised by the caller.  Arguments as
+ * aut_encode, without the workspace.  Keep aut_profile_enable off: its timing
+ * events are created on demand. */
+aut_status aut_encode_noalloc(const aut_config* cfg, const float* features, int32_t T_max,
+                              const int32_t* feature_lens, int32_t B, const void* packed,
+                              aut_dtype dtype, float* out, void* stream);
+
 /* Kernels only, for a plan already uploaded into `workspace`: no allocation,
  * no synchronisation, no host-to-device copy, so it can be captured in a HIP
  * graph and replayed.  Arguments as aut_encode. */

@@ -92,6 +92,8 @@ SIGNATURES = {
     "aut_mx_quantize": (c_int, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
     "aut_mx_matmul": (c_int, [c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_int32,
                               c_void_p, c_void_p]),
+    "aut_encode_noalloc": (c_int, [POINTER(AutConfig), c_void_p, c_int32, POINTER(c_int32), c_int32, c_void_p,
+                                    c_int, c_void_p, c_void_p]),
     "aut_layernorm": (c_int, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_float, c_int, c_void_p,
                                c_void_p, c_void_p]),
     "aut_profile_enable": (c_int, [c_int]),
@@ -306,6 +308,23 @@ def encode(cfg: AutConfig, features, feature_lens, packed, dtype, out=None, ws=N
     _check(lib().aut_encode(byref(cfg), _ptr(features), features.shape[2], arr, len(lens),
                             _ptr(packed), _dtype(dtype), _ptr(out), _ptr(ws), ws.numel(),
                             _stream_ptr(stream)))
+    return out, pl
+
+
+def encode_noalloc(cfg: AutConfig, features, feature_lens, packed, dtype, out=None, stream=None):
+    """aut_encode_noalloc: the whole forward on the library's device scratch
+    (no workspace argument); returns (out [T, output_dim] fp32, plan)."""
+    import torch
+    lens = [int(x) for x in feature_lens]
+    _check_features(features, cfg, len(lens))
+    pl = Plan(cfg, feature_lens)
+    if out is None:
+        out = torch.empty((pl.total_tokens, cfg.output_dim), dtype=torch.float32, device=features.device)
+    _check_f32(out, pl.total_tokens, cfg.output_dim, "out", features.device)
+    _check_bytes(packed, weights_bytes(cfg, dtype), "packed")
+    arr = (c_int32 * max(1, len(lens)))(*lens)
+    _check(lib().aut_encode_noalloc(byref(cfg), _ptr(features), features.shape[2], arr, len(lens),
+                                    _ptr(packed), _dtype(dtype), _ptr(out), _stream_ptr(stream)))
     return out, pl
 
 

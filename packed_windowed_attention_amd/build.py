@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libaut.so")
 
 SOURCES = ["aut_host.cpp", "k_stem.hip", "k_gemm128.hip", "k_gemm256.hip", "k_ln.hip", "k_attn.hip", "k_inject.hip",
-           "k_logmel.hip", "k_mx.hip"]
+           "k_logmel.hip", "k_mx.hip", "k_scratch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

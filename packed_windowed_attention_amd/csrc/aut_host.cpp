@@ -1003,6 +1003,54 @@ extern "C" aut_status aut_encode(const aut_config* cfg, const float* features, i
   return st;
 }
 
+extern "C" aut_status aut_encode_noalloc(const aut_config* cfg, const float* features, int32_t T_max,
+                                         const int32_t* feature_lens, int32_t B, const void* packed,
+                                         aut_dtype dt, float* out, void* stream) {
+  aut_plan_t* plan = nullptr;
+  aut_status st = aut_plan(cfg, feature_lens, B, &plan);
+  if (st != AUT_OK) return st;
+  st = check_dtype(*cfg, dt);
+  // the size check is host arithmetic and comes before any HIP call
+  if (st == AUT_OK) {
+    const size_t need = ws_layout(*plan, dt).total;
+    if (need > aut::scratch_bytes())
+      st = fail(AUT_ERR_WORKSPACE_TOO_SMALL,
+                "this batch needs %zu bytes of device scratch; aut_encode_noalloc holds %zu "
+                "(smaller batches, or a smaller conv_chunksize, fit)",
+                need, aut::scratch_bytes());
+  }
+  void* ws = nullptr;
+  if (st == AUT_OK && plan->total > 0) {
+    hipError_t e = aut::scratch_ptr(&ws);
+    if (e != hipSuccess) st = fail(AUT_ERR_HIP, "device scratch lookup failed: %s", hipGetErrorString(e));
+  }
+  WsLayout W;
+  if (st == AUT_OK && plan->total > 0) {
+    st = check_common(cfg, plan, dt, packed, ws, aut::scratch_bytes(), &W);
+    if (st == AUT_OK) st = check_features(features, T_max, *plan);
+    if (st == AUT_OK && !out) st = fail(AUT_ERR_INVALID_ARG, "out is NULL");
+  }
+  if (st == AUT_OK && plan->total > 0) {
+    // the plan tables straight from the plan's host memory (pageable: the
+    // runtime has consumed the source when each copy returns), no staging
+    hipStream_t s = (hipStream_t)stream;
+    char* d = (char*)ws;
+    hipError_t e = hipMemcpyAsync(d + W.chunks, plan->chunks.data(), plan->chunks.size() * sizeof(aut_chunk),
+                                  hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(d + W.rowmap, plan->rowmap.data(), plan->rowmap.size() * 4, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(d + W.cu, plan->cu.data(), plan->cu.size() * 4, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(d + W.worder, plan->worder.data(), plan->worder.size() * 4, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) st = fail(AUT_ERR_HIP, "plan upload failed: %s", hipGetErrorString(e));
+  }
+  if (st == AUT_OK && plan->total > 0)
+    st = aut_encode_planned(cfg, plan, features, T_max, packed, dt, out, ws, aut::scratch_bytes(), stream);
+  aut_plan_destroy(plan);
+  return st;
+}
+
 // ---------------------------------------------------------------------------
 // incremental (streaming) encode of one request
 // ---------------------------------------------------------------------------

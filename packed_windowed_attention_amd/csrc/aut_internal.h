@@ -40,6 +40,11 @@ hipError_t launch_logmel(const float* audio, long s_max, const int* lens_dev, in
 hipError_t launch_inject(const float* audio, const int* rows, long n, int dim, void* dst,
                          long dst_rows, aut_dtype dt, hipStream_t s);
 
+// The device scratch of aut_encode_noalloc: its size, and this device's
+// address of it (looked up on the first call per device, then cached).
+size_t scratch_bytes();
+hipError_t scratch_ptr(void** ptr);
+
 // Per-launch timing hooks (no-ops unless aut_profile_enable(1)).
 void prof_begin(hipStream_t s);
 void prof_end(hipStream_t s, aut_kernel_class cls, double flops, double bytes);

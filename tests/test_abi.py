@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = aut.lib()
     names = declared_functions()
-    assert len(names) == len(aut.SIGNATURES) == 30
+    assert len(names) == len(aut.SIGNATURES) == 31
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(aut.SIGNATURES), "binding and header disagree"
@@ -309,3 +309,16 @@ def test_mx_scale_layout_reindex():
     for r in (0, 15, 16, 36):
         for kb in range(K // 32):
             assert rm[r, kb] == flat[((r // 16) * (K // 128) + kb // 4) * 64 + (kb % 4) * 16 + r % 16]
+
+
+def test_encode_noalloc_rejects_a_batch_past_its_scratch():
+    """aut_encode_noalloc refuses, before any GPU call, a batch whose
+    workspace exceeds the library's device scratch, naming both sizes."""
+    cfg = aut.config(si.model_config("wide"), conv_chunksize=500)
+    lens = (ctypes.c_int32 * 1)(120000)          # 1200 s of audio: several GiB of workspace
+    fake = ctypes.c_void_p(256)
+    st = aut.lib().aut_encode_noalloc(ctypes.byref(cfg), fake, 120000, lens, 1, fake,
+                                      aut.DTYPES["bf16"], fake, None)
+    msg = aut.lib().aut_last_error().decode()
+    assert aut.STATUS.get(st) == "AUT_ERR_WORKSPACE_TOO_SMALL", (st, msg)
+    assert "device scratch" in msg and str(256 << 20) in msg
