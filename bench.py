@@ -209,6 +209,44 @@ def graph_rate(aut, torch, cfg, pl, fd, packed, dtype, eager_out, steps, audio_s
                     "outside; wall time per replay between two synchronisations"}
 
 
+def workload_rate(aut, torch, name, steps):
+    """Another full-size workload of the same model (long: one 1200 s request;
+    conc: 512 log-normal requests), its own seeded inputs and parameters:
+    eager aut_encode steps (plan, upload, kernels) and the forward captured
+    once in a HIP graph with the plan built and uploaded once outside (the
+    fixed-plan replay), each timed between two synchronisations."""
+    cfg_d, lens, feats, P = si.workload(name)
+    cfg_d = dict(cfg_d, conv_chunksize=max(cfg_d["conv_chunksize"], 4096))
+    dtype = cfg_d["dtype"]
+    cfg = aut.config(cfg_d)
+    dev = {k: torch.from_numpy(v).cuda() for k, v in P.items()}
+    packed = aut.weights_pack(cfg, dev, dtype)
+    del dev
+    fd = torch.from_numpy(feats).cuda()
+    pl = aut.plan(cfg, lens)
+    T = pl.total_tokens
+    audio_s = float(np.sum(lens)) / 100.0
+    ws = aut.workspace(cfg, pl, dtype)
+    out = torch.empty((T, cfg.output_dim), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        aut.encode(cfg, fd, lens, packed, dtype, out=out, ws=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        aut.encode(cfg, fd, lens, packed, dtype, out=out, ws=ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / steps
+    del ws
+    res = {"workload": f"{name}: {DESCR[name]}", "requests": int(len(lens)), "total_tokens": int(T),
+           "audio_seconds": audio_s, "n_windows": int(pl.n_windows), "steps": steps,
+           "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "audio_s_per_s": audio_s / (ms / 1e3),
+           "dtype": dtype}
+    res["graph_replay"] = graph_rate(aut, torch, cfg, pl, fd, packed, dtype, out, steps, audio_s)
+    del out, packed, fd
+    torch.cuda.empty_cache()
+    return res
+
+
 def stream_latency(aut, torch, cfg, packed, dtype, feats, steps, append=100):
     """Incremental encode of one live request (the workload's first request's
     mel, repeated as needed) receiving `append` frames per step: each step
@@ -352,6 +390,8 @@ def main():
                     help="1 s appends timed for the incremental-encode latency (0: skip)")
     ap.add_argument("--graph-steps", type=int, default=10,
                     help="replays of the forward captured in a HIP graph (0: skip)")
+    ap.add_argument("--other-steps", type=int, default=5,
+                    help="steps of the long and conc workloads, eager and as a fixed-plan graph replay (0: skip)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without per-launch HIP events (no roofline)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -363,7 +403,7 @@ def main():
     args = ap.parse_args()
     if args.traffic_summary:
         cmds = [f"rocprofv3 --pmc {c} -f csv -d <out> -o wide -- python <repo>/bench.py --steps 1 --warmup 0 "
-                "--no-cpu-baseline --no-kernel-events --fp8-steps 0 --stream-steps 0"
+                "--no-cpu-baseline --no-kernel-events --fp8-steps 0 --stream-steps 0 --other-steps 0"
                 for c in ("FETCH_SIZE", "WRITE_SIZE")]
         cmds += [f"rocprofv3 --pmc {c} -f csv -d <out> -o copy -- python <repo>/bench.py --calibrate-copy "
                  f"{args.calibrate_mib}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
@@ -516,6 +556,13 @@ def main():
         res["graph_replay"] = graph_rate(aut, torch, cfg, pl, fd, packed, dtype, out, args.graph_steps, audio_s)
         log(f"graph replay: {res['graph_replay']['ms_per_step']:.3f} ms/step, "
             f"bit-identical to eager: {res['graph_replay']['bit_identical_to_eager']}")
+    if args.other_steps > 0 and name == "wide":
+        res["other_workloads"] = []
+        for other in ("long", "conc"):
+            r = workload_rate(aut, torch, other, args.other_steps)
+            res["other_workloads"].append(r)
+            log(f"{other}: {r['ms_per_step']:.2f} ms/step eager, {r['graph_replay']['ms_per_step']:.2f} ms "
+                f"graph replay, {r['graph_replay']['tokens_per_s'] / 1e3:.0f} k tokens/s")
     res["logmel"] = logmel_rate(aut, torch, lens)
     log(f"logmel: {res['logmel']['ms']:.3f} ms for {res['logmel']['audio_seconds']:.0f} s of audio")
     res["inject"] = inject_rate(aut, torch, out)
