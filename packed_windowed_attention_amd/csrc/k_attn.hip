@@ -7,15 +7,17 @@
 // section 3: is_causal = False inside each cu_seqlens segment).
 //
 // One workgroup per (window, head).  The window's K (row-major) and V
-// (transposed) live in LDS, zero past the window's end, so padded keys
-// contribute exactly nothing and no row of another window is ever read.  Each
-// wave takes 16 queries at a time and computes S^T = K Q^T on the matrix
-// cores: a lane then holds the scores of one query (its column) for 16 keys
-// per tile, which is exactly the B-operand layout of the second product
-// O^T = V^T P^T, so P never leaves registers.  The softmax reductions over
-// keys run within a lane and across the four lane groups with wavefront
-// shuffles.  Windows are visited longest first (the plan's order) so short
-// tail windows fill the end of the grid.
+// (transposed) live in LDS, zero past the window's end (loads go through a
+// buffer descriptor that covers the window's rows only, so a load past its end
+// reads zero and no row of another window is ever read).  Each wave takes 16
+// queries at a time and computes S^T = K Q^T on the matrix cores: a lane then
+// holds the scores of one query (its column) for 16 keys per tile, which is
+// exactly the B-operand layout of the second product O^T = V^T P^T, so P never
+// leaves registers.  Key tiles that hold only padding are skipped and only
+// tiles that hold both real and padded keys are masked.  The softmax
+// reductions over keys run within a lane and across the four lane groups with
+// lane-swap instructions.  Windows are visited longest first (the plan's
+// order) so short tail windows fill the end of the grid.
 #include "aut_internal.h"
 #include "device_common.h"
 
@@ -77,6 +79,27 @@ __device__ __forceinline__ void store_quad(float* p, float a, float b, float c, 
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 
+// Reductions across the lane groups of a query's scores (lanes l, l ^ 16,
+// l ^ 32, l ^ 48): v_permlane16_swap / v_permlane32_swap exchange halves of
+// the wavefront in the vector unit, so the pair's two values sit in the two
+// results of one instruction, in every lane (no LDS round trip).
+__device__ __forceinline__ float pair_max16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // MX-fp8 output of a query row's 64 head columns: a lane holds columns
 // 16 dt + 4 g + r (dt = 0..3, r = 0..3) of its query, so each 32-column block
 // (dt = 0, 1 or dt = 2, 3) is spread over the four lanes of the query's row
@@ -103,48 +126,53 @@ __device__ __forceinline__ void store_row_mx(uint8_t* orow, uint8_t* osc, int ro
   }
 }
 
-template <typename T, bool MX>
-__global__ __launch_bounds__(ATT_THREADS) void attn_kernel(const T* __restrict__ qkv,
-                                                          void* __restrict__ o_,
-                                                          const int* __restrict__ cu,
-                                                          const int* __restrict__ worder, int H,
-                                                          int d, uint8_t* __restrict__ osc) {
-  constexpr int E = UnitElems<T>::value;  // elements per 16-byte unit
-  constexpr int UR = 64 / E;              // units per head row
-  constexpr int VS = VtStride<T>::value;
-  typedef typename FragOf<T>::type Frag;
-  __shared__ u32x4_t Ks[LMAX * UR];
-  __shared__ T Vt[64 * VS];
+// One (window, head) item's operands in registers: thread t holds unit
+// u = t % UR of the RPT consecutive key rows from RPT * (t / UR) (K and V),
+// and each wave the Q fragments of its query tiles wave and wave + 4.
+template <typename T>
+struct ItemRegs {
+  static constexpr int E = UnitElems<T>::value;           // elements per 16-byte unit
+  static constexpr int UR = 64 / E;                        // units per head row
+  static constexpr int RPT = LMAX * UR / ATT_THREADS;     // key rows per thread: 4 (bf16), 8 (fp32)
+  static constexpr int QU = E == 8 ? 2 : 4;                // Q units per lane per query tile
+  u32x4_t k[RPT], v[RPT];
+  u32x4_t q[2][QU];
+};
 
-  const int tid = threadIdx.x;
+struct Item {
+  int s0, L, h;
+};
+
+__device__ __forceinline__ Item item_of(int item, const int* __restrict__ cu,
+                                        const int* __restrict__ worder, int H) {
+  const int wi = item / H;
+  const int w = worder[wi];
+  Item it;
+  it.h = item - wi * H;
+  it.s0 = cu[w];
+  it.L = cu[w + 1] - it.s0;
+  return it;
+}
+
+// The rows of an item's window as a buffer: a load past the window's last row
+// returns zero, so the padded keys and queries need no branch (a branch per
+// load made the compiler wait for each load before issuing the next).
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t window_rsrc(const T* __restrict__ qkv, const Item& it,
+                                                             int d) {
+  const size_t ld = 3 * (size_t)d;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(qkv + (size_t)it.s0 * ld), (short)0,
+                                           (int)((size_t)it.L * ld * sizeof(T)), 0x00020000);
+}
+
+template <typename T>
+__device__ __forceinline__ void load_q(ItemRegs<T>& r, const T* __restrict__ qkv, const Item& it,
+                                       int d, int tid) {
+  constexpr int E = ItemRegs<T>::E, QU = ItemRegs<T>::QU;
   const int lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 15, g = lane >> 4;
-  const int w = worder[blockIdx.x / H];
-  const int h = blockIdx.x - (blockIdx.x / H) * H;
-  const int s0 = cu[w];
-  const int L = cu[w + 1] - s0;
-  const size_t ld = 3 * (size_t)d;
-  const T* qb = qkv + (size_t)s0 * ld + (size_t)h * 64;
-  const T* kb = qb + d;
-  const T* vb = qb + 2 * (size_t)d;
-
-  // Every global load of the workgroup is issued before any is used: thread t
-  // takes unit u = t % UR of the RPT consecutive key rows starting at
-  // RPT * (t / UR) (K and V), and each wave the Q fragments of its query tiles
-  // wave and wave + 4.  Then K goes to LDS unit by unit and V transposed, RPT
-  // rows at a time (one 8- or 32-byte write per element of the unit).
-  constexpr int RPT = LMAX * UR / ATT_THREADS;  // key rows per thread: 4 (bf16), 8 (fp32)
-  const int ku = tid % UR;
-  const int kj0 = RPT * (tid / UR);
-  u32x4_t kreg[RPT], vreg[RPT];
-#pragma unroll
-  for (int r = 0; r < RPT; ++r) {
-    const int j = kj0 + r;
-    kreg[r] = j < L ? ldg_unit(kb + (size_t)j * ld + ku * E) : zero_unit();
-    vreg[r] = j < L ? ldg_unit(vb + (size_t)j * ld + ku * E) : zero_unit();
-  }
-  constexpr int QU = E == 8 ? 2 : 4;  // Q units per lane per query tile
-  u32x4_t qreg[2][QU];
+  const unsigned ldb = 3u * (unsigned)d * sizeof(T);
+  const __amdgpu_buffer_rsrc_t rs = window_rsrc(qkv, it, d);
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int i = (wave + 4 * q) * 16 + lrow;
@@ -152,19 +180,49 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_kernel(const T* __restrict__
     for (int s = 0; s < QU; ++s) {
       // bf16: units 4 s' + g of k-half s'; fp32: units 8 s' + 2 g (+1)
       const int u = E == 8 ? 4 * s + g : 8 * (s >> 1) + 2 * g + (s & 1);
-      qreg[q][s] = i < L ? ldg_unit(qb + (size_t)i * ld + u * E) : zero_unit();
+      const unsigned off = (unsigned)i * ldb + (unsigned)((it.h * 64 + u * E) * sizeof(T));
+      r.q[q][s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
     }
   }
+}
+
+template <typename T>
+__device__ __forceinline__ void load_item(ItemRegs<T>& r, const T* __restrict__ qkv, const Item& it,
+                                          int d, int tid) {
+  constexpr int E = ItemRegs<T>::E, UR = ItemRegs<T>::UR, RPT = ItemRegs<T>::RPT;
+  const unsigned ldb = 3u * (unsigned)d * sizeof(T);
+  const __amdgpu_buffer_rsrc_t rs = window_rsrc(qkv, it, d);
+  const int ku = tid % UR;
+  const int kj0 = RPT * (tid / UR);
+  const unsigned koff = (unsigned)((d + it.h * 64 + ku * E) * sizeof(T));
+  const unsigned voff = koff + (unsigned)(d * sizeof(T));
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) Ks[(kj0 + r) * UR + kswz<T>(ku, kj0 + r)] = kreg[r];
+  for (int j = 0; j < RPT; ++j) {
+    const unsigned row = (unsigned)(kj0 + j) * ldb;
+    r.k[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, row + koff, 0, 0));
+    r.v[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, row + voff, 0, 0));
+  }
+  load_q(r, qkv, it, d, tid);
+}
+
+// K to LDS unit by unit, V transposed, RPT rows at a time (one 8- or 32-byte
+// write per element of the unit).
+template <typename T>
+__device__ __forceinline__ void stage_item(const ItemRegs<T>& r, u32x4_t* Ks, T* Vt, int tid) {
+  constexpr int E = ItemRegs<T>::E, UR = ItemRegs<T>::UR, RPT = ItemRegs<T>::RPT;
+  constexpr int VS = VtStride<T>::value;
+  const int ku = tid % UR;
+  const int kj0 = RPT * (tid / UR);
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) Ks[(kj0 + j) * UR + kswz<T>(ku, kj0 + j)] = r.k[j];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     T col[RPT];
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) {
+    for (int j = 0; j < RPT; ++j) {
       T tmp[E];
-      __builtin_memcpy(tmp, &vreg[r], 16);
-      col[r] = tmp[e];
+      __builtin_memcpy(tmp, &r.v[j], 16);
+      col[j] = tmp[e];
     }
     T* dst = &Vt[(ku * E + e) * VS + kj0];
     if (E == 8) {
@@ -178,105 +236,170 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_kernel(const T* __restrict__
       reinterpret_cast<u32x4_t*>(dst)[1] = w4[1];
     }
   }
-  __syncthreads();
+}
 
-  // scores in log2 units: softmax(s / 8) = 2^(s log2(e) / 8 - max) / sum
-  const float c = 0.125f * 1.44269504088896341f;
+// One 16-query tile of an item: the scores of NKT key tiles (the rest hold
+// only padded keys and are skipped: their probabilities are zero), masked in
+// every tile (MASK_ALL, short windows) or in the last one only.  A lane ends
+// up with one query's scores (its column of S^T), so the softmax reductions
+// are in-lane plus two wavefront shuffles.
+template <typename T, bool MX, int NKT, bool MASK_ALL>
+__device__ __forceinline__ void query_tile(const u32x4_t* Ks, const T* Vt,
+                                           const u32x4_t (&qr)[ItemRegs<T>::QU], int qt,
+                                           const Item& it, void* __restrict__ o_, int d,
+                                           uint8_t* __restrict__ osc, int lane) {
+  constexpr int E = ItemRegs<T>::E, UR = ItemRegs<T>::UR;
+  constexpr int VS = VtStride<T>::value;
+  typedef typename FragOf<T>::type Frag;
+  const int lrow = lane & 15, g = lane >> 4;
+  const int L = it.L;
+  const int i = qt * 16 + lrow;
+  Frag qf[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int it = wave + 4 * q;
-    if (it * 16 >= L) break;
-    const int i = it * 16 + lrow;
-    Frag qf[2];
+  for (int s = 0; s < 2; ++s) {
+    if (E == 8) frag_from_units(qf[s], qr[s], zero_unit());
+    else frag_from_units(qf[s], qr[2 * s], qr[2 * s + 1]);
+  }
+  // S^T = K Q^T: every fragment read is issued ahead of the matrix
+  // instructions that use it.  (The row index is made opaque per query tile:
+  // otherwise the compiler keeps one tile's K fragments live for the next and
+  // runs out of registers.)
+  int krow = lrow;
+  asm volatile("" : "+v"(krow));
+  Frag kf[NKT][2];
+#pragma unroll
+  for (int jt = 0; jt < NKT; ++jt) {
+    const int jr = jt * 16 + krow;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      if (E == 8) frag_from_units(qf[s], qreg[q][s], zero_unit());
-      else frag_from_units(qf[s], qreg[q][2 * s], qreg[q][2 * s + 1]);
-    }
-    // S^T = K Q^T over all LMAX key rows (rows past the window are zero in LDS
-    // and masked below): straight-line code, so every fragment read is issued
-    // ahead of the matrix instructions that use it
-    Frag kf[8][2];
-#pragma unroll
-    for (int jt = 0; jt < 8; ++jt) {
-      const int jr = jt * 16 + lrow;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (E == 8) {
-          frag_from_units(kf[jt][s], Ks[jr * UR + kswz<T>(4 * s + g, jr)], zero_unit());
-        } else {
-          const int u = 8 * s + 2 * g;
-          frag_from_units(kf[jt][s], Ks[jr * UR + kswz<T>(u, jr)], Ks[jr * UR + kswz<T>(u + 1, jr)]);
-        }
+      if (E == 8) {
+        frag_from_units(kf[jt][s], Ks[jr * UR + kswz<T>(4 * s + g, jr)], zero_unit());
+      } else {
+        const int u = 8 * s + 2 * g;
+        frag_from_units(kf[jt][s], Ks[jr * UR + kswz<T>(u, jr)], Ks[jr * UR + kswz<T>(u + 1, jr)]);
       }
-    }
-    float t[8][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int jt = 0; jt < 8; ++jt) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      mma16_k32(acc, kf[jt][0], qf[0]);
-      mma16_k32(acc, kf[jt][1], qf[1]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = jt * 16 + 4 * g + r;
-        t[jt][r] = j < L ? acc[r] * c : -INFINITY;
-        mx = fmaxf(mx, t[jt][r]);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    float sum = 0.f;
-#pragma unroll
-    for (int jt = 0; jt < 8; ++jt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        t[jt][r] = __builtin_amdgcn_exp2f(t[jt][r] - mx);  // masked keys: 2^-inf = 0
-        sum += t[jt][r];
-      }
-    sum += __shfl_xor(sum, 16, 64);
-    sum += __shfl_xor(sum, 32, 64);
-
-    // O^T = V^T P^T, V^T fragments read ahead in two batches of 8
-    f32x4_t oacc[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      Frag vf[2][4];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const T* vrow = Vt + (dt * 16 + lrow) * VS + 32 * (2 * half + u) + 4 * g;
-          frag_v(vf[u][dt], vrow, vrow + 16);
-        }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int tt = 2 * half + u;
-        Frag pf;
-        frag_p(pf, t[2 * tt], t[2 * tt + 1]);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) mma16_k32(oacc[dt], vf[u][dt], pf);
-      }
-    }
-    const float inv = __builtin_amdgcn_rcpf(sum);
-    if constexpr (MX) {
-      float v[4][4];
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[dt][r] = oacc[dt][r] * inv;
-      store_row_mx((uint8_t*)o_ + (size_t)(s0 + i) * d + (size_t)h * 64, osc, s0 + i, h * 64, d, g,
-                   v, i < L);
-    } else if (i < L) {
-      T* orow = (T*)o_ + (size_t)(s0 + i) * d + (size_t)h * 64;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        store_quad(orow + dt * 16 + 4 * g, oacc[dt][0] * inv, oacc[dt][1] * inv,
-                   oacc[dt][2] * inv, oacc[dt][3] * inv);
     }
   }
+  // raw scores; padded keys -inf
+  float t[8][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int jt = 0; jt < NKT; ++jt) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    mma16_k32(acc, kf[jt][0], qf[0]);
+    mma16_k32(acc, kf[jt][1], qf[1]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = jt * 16 + 4 * g + r;
+      t[jt][r] = (MASK_ALL || jt == NKT - 1) && j >= L ? -INFINITY : acc[r];
+      mx = fmaxf(mx, t[jt][r]);
+    }
+  }
+  mx = pair_max16(mx);
+  mx = pair_max32(mx);
+  // softmax(s / 8) = 2^(s c - max c) / sum with c = log2(e) / 8; c > 0, so the
+  // scaled maximum is the maximum of the scaled scores
+  const float c = 0.125f * 1.44269504088896341f;
+  const float mc = mx * c;
+  float sum = 0.f;
+#pragma unroll
+  for (int jt = 0; jt < 8; ++jt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (jt < NKT) {
+        t[jt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[jt][r], c, -mc));  // -inf: 0
+        sum += t[jt][r];
+      } else {
+        t[jt][r] = 0.f;
+      }
+    }
+  sum = pair_sum16(sum);
+  sum = pair_sum32(sum);
+
+  // O^T = V^T P^T, V^T fragments read ahead in two batches of 8
+  f32x4_t oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    Frag vf[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const T* vrow = Vt + (dt * 16 + lrow) * VS + 32 * (2 * half + u) + 4 * g;
+        frag_v(vf[u][dt], vrow, vrow + 16);
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tt = 2 * half + u;
+      Frag pf;
+      frag_p(pf, t[2 * tt], t[2 * tt + 1]);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) mma16_k32(oacc[dt], vf[u][dt], pf);
+    }
+  }
+  const float inv = __builtin_amdgcn_rcpf(sum);
+  const int s0 = it.s0, h = it.h;
+  if constexpr (MX) {
+    float v[4][4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[dt][r] = oacc[dt][r] * inv;
+    store_row_mx((uint8_t*)o_ + (size_t)(s0 + i) * d + (size_t)h * 64, osc, s0 + i, h * 64, d, g, v,
+                 i < L);
+  } else if (i < L) {
+    T* orow = (T*)o_ + (size_t)(s0 + i) * d + (size_t)h * 64;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      store_quad(orow + dt * 16 + 4 * g, oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv,
+                 oacc[dt][3] * inv);
+  }
+}
+
+// One item's attention from LDS (K, transposed V) and the Q fragments in
+// registers: each wave its query tiles wave and wave + 4.  Windows of 97 to
+// 112 tokens (the common full window) skip the eighth key tile; windows of
+// more than 112 mask the eighth only; shorter ones mask every tile.
+template <typename T, bool MX>
+__device__ __forceinline__ void compute_item(const u32x4_t* Ks, const T* Vt,
+                                             const u32x4_t (&qreg)[2][ItemRegs<T>::QU],
+                                             const Item& it, void* __restrict__ o_, int d,
+                                             uint8_t* __restrict__ osc, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int qt = wave + 4 * q;
+    if (qt * 16 >= it.L) break;
+    if (it.L > 112)
+      query_tile<T, MX, 8, false>(Ks, Vt, qreg[q], qt, it, o_, d, osc, lane);
+    else if (it.L > 96)
+      query_tile<T, MX, 7, false>(Ks, Vt, qreg[q], qt, it, o_, d, osc, lane);
+    else
+      query_tile<T, MX, 8, true>(Ks, Vt, qreg[q], qt, it, o_, d, osc, lane);
+  }
+}
+
+// One workgroup per (window, head) item, items window-major in the plan's
+// window order (longest first, so short tail windows fill the end of the
+// grid): every load issued at once, K and V to LDS, then the matrix work.
+template <typename T, bool MX>
+__global__ __launch_bounds__(ATT_THREADS)
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 2))) void attn_kernel(
+    const T* __restrict__ qkv, void* __restrict__ o_, const int* __restrict__ cu,
+    const int* __restrict__ worder, int H, int d, uint8_t* __restrict__ osc) {
+  constexpr int UR = ItemRegs<T>::UR;
+  constexpr int VS = VtStride<T>::value;
+  __shared__ u32x4_t Ks[LMAX * UR];
+  __shared__ T Vt[64 * VS];
+  const int tid = threadIdx.x;
+  ItemRegs<T> r;
+  const Item it = item_of((int)blockIdx.x, cu, worder, H);
+  load_item(r, qkv, it, d, tid);
+  stage_item(r, Ks, Vt, tid);
+  __syncthreads();
+  compute_item<T, MX>(Ks, Vt, r.q, it, o_, d, osc, tid);
 }
 
 }  // namespace
