@@ -75,6 +75,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// a compile-time part index for the phase helpers of the MX-fp8 kernel
+template <int P> struct PartC { static constexpr int value = P; };
+
 // s_waitcnt lgkmcnt(0) alone, then a workgroup barrier: orders the LDS traffic
 // of the epilogue without waiting for the global stores in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -905,42 +908,157 @@ void gemm8w_f8_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
 
   const int lrow = lane & 15;
   const int g = lane >> 4;
-  auto step = [&](int kt, const u32x4_t* As_s, const u32x4_t* Bs_s, const unsigned* Sa_s,
-                  const unsigned* Sb_s, u32x4_t* As_n, u32x4_t* Bs_n, unsigned* Sa_n, unsigned* Sb_n)
-      __attribute__((always_inline)) {
-    wait_vmcnt<0>();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kt + 1 < KS) issue(kt + 1, As_n, Bs_n, Sa_n, Sb_n);
+  // Ping-pong schedule (convolution GEMMs on 256-column tiles; the lockstep
+  // loop below serves the rest), as in the bf16 eight-wave kernel: the two rows
+  // of waves, G0 (wm = 0) and G1 (wm = 1), run one phase apart, a phase being
+  // either the matrix instructions of one half of a step (row blocks 0..3 or
+  // 4..7, 20 instructions) or the fragment reads of the next half plus this
+  // wave's share of a step's loads, each phase ending at a barrier.  The
+  // weight fragments and scales of a step are read with its first half.
+  // Stage kt % 2 serves step kt; G1 issues its loads of step kt + 1 in phase 0
+  // of step kt and G0 in phase 3 of step kt - 1, after every reader of that
+  // stage is past it.  Each output still sums its k steps in increasing order.
+  i32x8_t wb[NTW], xa[4];
+  int sw[NTW], sx[4];
+  auto rd = [&](const u32x4_t* As_s, const u32x4_t* Bs_s, const unsigned* Sa_s, const unsigned* Sb_s,
+                auto part_c) __attribute__((always_inline)) {
+    constexpr int part = decltype(part_c)::value;
     // A_PLAIN: group wm * 8 + i, byte 64 i + lane; gathered: row wm * 128 + 16 i + lrow, byte g
     const uint8_t* sa = AMODE == A_PLAIN ? (const uint8_t*)Sa_s + wm * 512 + lane
                                          : (const uint8_t*)Sa_s + (wm * 128 + lrow) * 4 + g;
-    const uint8_t* sb = (const uint8_t*)Sb_s + wn * (WN * 4) + lane;
-    i32x8_t wb[NTW];
-    int sw[NTW];
+    if constexpr (part == 0) {
+      const uint8_t* sb = (const uint8_t*)Sb_s + wn * (WN * 4) + lane;
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int r = wn * WN + 16 * j + lrow;
-      wb[j] = units_to_i32x8(Bs_s[r * KU + swz(g, r)], Bs_s[r * KU + swz(g + 4, r)]);
-      sw[j] = sb[64 * j];
+      for (int j = 0; j < NTW; ++j) {
+        const int r = wn * WN + 16 * j + lrow;
+        wb[j] = units_to_i32x8(Bs_s[r * KU + swz(g, r)], Bs_s[r * KU + swz(g + 4, r)]);
+        sw[j] = sb[64 * j];
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = 4 * part + ii;
       const int r = wm * 128 + 16 * i + lrow;
-      const i32x8_t xa = units_to_i32x8(As_s[r * KU + swz(g, r)], As_s[r * KU + swz(g + 4, r)]);
-      const int sx = sa[64 * i];   // 64 bytes per 16 rows in both layouts
-#pragma unroll
-      for (int j = 0; j < NTW; ++j)
-        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb[j], xa, acc[j][i], 0, 0, 0,
-                                                                     sw[j], 0, sx);
+      xa[ii] = units_to_i32x8(As_s[r * KU + swz(g, r)], As_s[r * KU + swz(g + 4, r)]);
+      sx[ii] = sa[64 * i];   // 64 bytes per 16 rows in both layouts
     }
   };
+  auto mm = [&](auto part_c) __attribute__((always_inline)) {
+    constexpr int part = decltype(part_c)::value;
+    __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        acc[j][4 * part + ii] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            wb[j], xa[ii], acc[j][4 * part + ii], 0, 0, 0, sw[j], 0, sx[ii]);
+    // pin the phase's matrix instructions here: they touch no memory, so
+    // without a use the compiler sinks them past the barriers that follow
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) asm volatile("" : "+v"(acc[j][4 * part + ii]));
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto bar = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // s_waitcnt lgkmcnt(0) alone: this wave's fragment reads have returned
+  auto lgkm0 = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+  };
 
+  if constexpr (BN > 256 || AMODE != A_CONV) {
+    // The lockstep loop, one barrier per step.  256 x 320 tiles have no
+    // registers for the ping-pong's fragments next to the 160 accumulators;
+    // the ping-pong pays (conv GEMMs 4% faster) only on the convolution's long
+    // k loops: on the 256-column layer GEMMs it cost 18%, on conv_out 5%.
+    auto step = [&](int kt, const u32x4_t* As_s, const u32x4_t* Bs_s, const unsigned* Sa_s,
+                    const unsigned* Sb_s, u32x4_t* As_n, u32x4_t* Bs_n, unsigned* Sa_n, unsigned* Sb_n)
+        __attribute__((always_inline)) {
+      wait_vmcnt<0>();
+      bar();
+      if (kt + 1 < KS) issue(kt + 1, As_n, Bs_n, Sa_n, Sb_n);
+      const uint8_t* sa = AMODE == A_PLAIN ? (const uint8_t*)Sa_s + wm * 512 + lane
+                                           : (const uint8_t*)Sa_s + (wm * 128 + lrow) * 4 + g;
+      const uint8_t* sb = (const uint8_t*)Sb_s + wn * (WN * 4) + lane;
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int r = wn * WN + 16 * j + lrow;
+        wb[j] = units_to_i32x8(Bs_s[r * KU + swz(g, r)], Bs_s[r * KU + swz(g + 4, r)]);
+        sw[j] = sb[64 * j];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = wm * 128 + 16 * i + lrow;
+        const i32x8_t x = units_to_i32x8(As_s[r * KU + swz(g, r)], As_s[r * KU + swz(g + 4, r)]);
+        const int sxi = sa[64 * i];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb[j], x, acc[j][i], 0, 0, 0,
+                                                                       sw[j], 0, sxi);
+      }
+    };
+    issue(0, As0, Bs0, Sa0, Sb0);
+    for (int kt = 0; kt < KS; kt += 2) {
+      step(kt, As0, Bs0, Sa0, Sb0, As1, Bs1, Sa1, Sb1);
+      if (kt + 1 < KS) step(kt + 1, As1, Bs1, Sa1, Sb1, As0, Bs0, Sa0, Sb0);
+    }
+  } else {
   issue(0, As0, Bs0, Sa0, Sb0);
-  for (int kt = 0; kt < KS; kt += 2) {
-    step(kt, As0, Bs0, Sa0, Sb0, As1, Bs1, Sa1, Sb1);
-    if (kt + 1 < KS) step(kt + 1, As1, Bs1, Sa1, Sb1, As0, Bs0, Sa0, Sb0);
+  wait_vmcnt<0>();
+  bar();
+  // Both groups pass the same number of barriers: 1 + 4 per step.
+  if (wm == 0) {
+    rd(As0, Bs0, Sa0, Sb0, PartC<0>{});      // phase -1: read (0, h0), G0's loads of step 1
+    if (1 < KS) issue(1, As1, Bs1, Sa1, Sb1);
+    lgkm0();
+    bar();
+    auto g0step = [&](int kt, const u32x4_t* As_s, const u32x4_t* Bs_s, const unsigned* Sa_s,
+                      const unsigned* Sb_s, u32x4_t* As_n, u32x4_t* Bs_n, unsigned* Sa_n,
+                      unsigned* Sb_n) __attribute__((always_inline)) {
+      mm(PartC<0>{});                         // phase 0: (kt, h0)
+      bar();
+      rd(As_s, Bs_s, Sa_s, Sb_s, PartC<1>{}); // phase 1: read (kt, h1)
+      lgkm0();
+      bar();
+      mm(PartC<1>{});                         // phase 2: (kt, h1)
+      wait_vmcnt<0>();                        // this wave's loads of step kt + 1
+      bar();
+      if (kt + 1 < KS) rd(As_n, Bs_n, Sa_n, Sb_n, PartC<0>{});  // phase 3: read (kt + 1, h0), G0's loads of kt + 2
+      if (kt + 2 < KS) issue(kt + 2, (u32x4_t*)As_s, (u32x4_t*)Bs_s, (unsigned*)Sa_s, (unsigned*)Sb_s);
+      lgkm0();
+      bar();
+    };
+    for (int kt = 0; kt < KS; kt += 2) {
+      g0step(kt, As0, Bs0, Sa0, Sb0, As1, Bs1, Sa1, Sb1);
+      if (kt + 1 < KS) g0step(kt + 1, As1, Bs1, Sa1, Sb1, As0, Bs0, Sa0, Sb0);
+    }
+  } else {
+    bar();                                    // phase -1
+    auto g1step = [&](int kt, const u32x4_t* As_s, const u32x4_t* Bs_s, const unsigned* Sa_s,
+                      const unsigned* Sb_s, u32x4_t* As_n, u32x4_t* Bs_n, unsigned* Sa_n,
+                      unsigned* Sb_n) __attribute__((always_inline)) {
+      rd(As_s, Bs_s, Sa_s, Sb_s, PartC<0>{}); // phase 0: read (kt, h0), G1's loads of kt + 1
+      if (kt + 1 < KS) issue(kt + 1, As_n, Bs_n, Sa_n, Sb_n);
+      lgkm0();
+      bar();
+      mm(PartC<0>{});                         // phase 1: (kt, h0)
+      bar();
+      rd(As_s, Bs_s, Sa_s, Sb_s, PartC<1>{}); // phase 2: read (kt, h1)
+      lgkm0();
+      wait_vmcnt<0>();                        // this wave's loads of step kt + 1
+      bar();
+      mm(PartC<1>{});                         // phase 3: (kt, h1)
+      bar();
+    };
+    for (int kt = 0; kt < KS; kt += 2) {
+      g1step(kt, As0, Bs0, Sa0, Sb0, As1, Bs1, Sa1, Sb1);
+      if (kt + 1 < KS) g1step(kt + 1, As1, Bs1, Sa1, Sb1, As0, Bs0, Sa0, Sb0);
+    }
+  }
   }
 
   staged_epilogue<BN, WN, NT8, EPI>(p, m0, n0, wm, wn, tid, acc, As0, As1, Bs0, Bs1);
