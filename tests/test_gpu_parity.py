@@ -95,6 +95,26 @@ def test_window_sizes(n_window_infer, dtype):
     check(y, ref, dtype, f"window {13 * n_window_infer // 100} tokens")
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_attention_key_tile_paths(dtype):
+    """Windows on each side of the attention kernel's key-tile boundaries: 96
+    (every tile masked), 97 and 112 (the eighth key tile skipped, the seventh
+    masked), 113 and 117 (all eight tiles, the last masked), with 117-token
+    windows (9 chunks) and single-chunk leftovers; the whole output against the
+    oracle."""
+    cfg_d = small_cfg(dtype, n_window_infer=900)
+    lens = np.array([740, 748, 864, 872, 900, 1764, 1])
+    feats = si.mel_features(lens, seed=67)
+    P = si.params(cfg_d, seed=67, std=0.05)
+    print(f"case: key-tile paths, {dtype}", flush=True)
+    y, pl = forward(cfg_d, lens, feats, P)
+    ref, opl = oracle.forward(feats, lens, P, cfg_d)
+    assert pl.copy()[1] == opl["cu_seqlens"]
+    wl = sorted(set(np.diff(opl["cu_seqlens"]).tolist()))
+    assert {96, 97, 112, 113, 117, 1} <= set(wl), wl
+    check(y, ref, dtype, f"key-tile paths, windows {wl}")
+
+
 @pytest.mark.parametrize("n_window,n_window_infer,dtype", [(25, 400, "fp32"), (60, 960, "bf16"),
                                                           (10, 160, "bf16")])
 def test_chunk_sizes(n_window, n_window_infer, dtype):
