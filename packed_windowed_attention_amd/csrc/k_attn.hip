@@ -408,6 +408,9 @@ hipError_t launch_attention(const void* qkv, void* o, const int* cu, const int* 
                             int n_windows, int H, int d, aut_dtype dt, hipStream_t s,
                             uint8_t* o_scales) {
   if (n_windows <= 0) return hipSuccess;
+  // a window's rows must fit a buffer descriptor's 32-bit byte range
+  if ((size_t)LMAX * 3 * (size_t)d * (dt == AUT_FP32 ? 4 : 2) >= ((size_t)1 << 31))
+    return hipErrorInvalidValue;
   dim3 grid(n_windows * H);
   if (dt == AUT_FP8) {
     if (d % 128 || !o_scales) return hipErrorInvalidValue;
