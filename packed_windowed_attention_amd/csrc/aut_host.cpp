@@ -521,6 +521,10 @@ struct WsLayout {
   size_t chunks, rowmap, cu, worder;
   size_t a1, a2, a3;
   size_t a1_s, a2_s, a3_s;  // AUT_FP8_CONV: MX scales of the conv-stem activations
+  // a3 holds every chunk's conv3 output, so that conv_out runs once over all
+  // tokens (a full grid) rather than once per conv batch; false when that
+  // buffer would pass the 2 GiB of the GEMM's 32-bit gather offsets
+  bool a3_all;
   size_t x, xn, qkv, o, h;
   size_t xn_s, o_s, h_s;  // AUT_FP8: MX scales of xn, o and h
   size_t total;
@@ -553,15 +557,17 @@ WsLayout ws_layout(const aut_plan_t& p, aut_dtype dt) {
   W.rowmap = take(T * 4);
   W.cu = take((nw + 1) * 4);
   W.worder = take(nw * 4);
+  W.a3_all = nch * g.h3 * g.w3 * cs < ((size_t)1 << 31);
+  const size_t n3 = W.a3_all ? nch : nb;  // chunks held in a3
   W.a1 = take(nb * g.h1 * g.w1 * cs);
   W.a2 = take(nb * g.h2 * g.w2 * cs);
-  W.a3 = take(nb * g.h3 * g.w3 * cs);
+  W.a3 = take(n3 * g.h3 * g.w3 * cs);
   W.a1_s = W.a2_s = W.a3_s = 0;
   if (f8c) {
     const size_t spp = (size_t)conv_cp(g) / 32;  // scale bytes per pixel
     W.a1_s = take(nb * g.h1 * g.w1 * spp);
     W.a2_s = take(nb * g.h2 * g.w2 * spp);
-    W.a3_s = take(nb * g.h3 * g.w3 * spp);
+    W.a3_s = take(n3 * g.h3 * g.w3 * spp);
   }
   W.x = take(T * g.d * 4);
   W.xn = take(T * g.d * es);
@@ -734,6 +740,43 @@ aut_status run_frontend(const Ctx& c, const float* feat, int T_max, float* hidde
   const int nch = (int)p.chunks.size();
   const int* d_chunks = (const int*)(c.ws + W.chunks);
   const int* d_rowmap = (const int*)(c.ws + W.rowmap);
+  // conv_out + positions: tokens [r0, r1), whose conv3 rows are chunks
+  // [first, first + count) of a3
+  auto conv_out = [&](int r0, int r1, int first, int count) -> aut_status {
+    if (r1 <= r0) return AUT_OK;
+    aut::GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = c.ws + W.a3;
+    a.B = c.pk + P.conv_out_w;
+    a.M = r1 - r0;
+    a.N = g.d;
+    a.rowmap = d_rowmap + r0;
+    a.rowmap_base = first * g.w3;
+    a.tpc = g.w3;
+    a.bias = p.cfg.conv_out_bias ? pk_at<float>(c, P.conv_out_b) : nullptr;
+    a.out = hidden + (size_t)r0 * g.d;
+    a.ldo = g.d;
+    a.pe = pk_at<float>(c, P.pe);
+    if (f8) {
+      a.lda = (long)g.h3 * cp;
+      a.ldb = (long)g.h3 * cp;
+      a.K = g.h3 * cp;
+      a.a_bytes = (size_t)count * g.w3 * g.h3 * cp;
+      a.a_scale = (const uint8_t*)(c.ws + W.a3_s);
+      a.a_scale_ld = g.h3 * cp / 32;
+      a.a_scale_bytes = (size_t)count * g.w3 * g.h3 * (cp / 32);
+      a.b_scale = (const uint8_t*)(c.pk + P.conv_out_s);
+      const double bytes = ((double)a.M * a.K + (double)g.d * a.K) * (1.0 + 1.0 / 32) +
+                           (double)a.M * g.d * 4;
+      return gemm_f8(c, AUT_K_CONV_OUT, a, aut::A_ROWMAP, aut::EPI_PE, bytes);
+    }
+    a.lda = (long)g.h3 * g.C;
+    a.ldb = (long)g.h3 * g.C;
+    a.K = g.h3 * g.C;
+    a.a_bytes = (size_t)count * g.w3 * g.h3 * g.C * es;
+    const double bytes = ((double)a.M * a.K + (double)g.d * a.K) * es + (double)a.M * g.d * 4;
+    return gemm(c, AUT_K_CONV_OUT, a, aut::A_ROWMAP, aut::EPI_PE, bytes);
+  };
   for (int c0 = 0; c0 < nch; c0 += W.nb) {
     const int n = std::min(W.nb, nch - c0);
     // conv1 + GELU
@@ -759,7 +802,9 @@ aut_status run_frontend(const Ctx& c, const float* feat, int T_max, float* hidde
       a.M = n * a.hout * a.wout;
       a.N = g.C;
       a.bias = pk_at<float>(c, l2 ? P.conv2_b : P.conv3_b);
-      a.out = c.ws + (l2 ? W.a2 : W.a3);
+      // conv3 writes at the batch's chunk offset when a3 holds every chunk
+      const size_t a3_first = W.a3_all ? (size_t)c0 * g.h3 * g.w3 : 0;  // pixel offset
+      a.out = c.ws + (l2 ? W.a2 : W.a3 + a3_first * cs);
       aut_status st;
       if (f8) {
         a.cin = cp;
@@ -772,7 +817,7 @@ aut_status run_frontend(const Ctx& c, const float* feat, int T_max, float* hidde
         a.b_scale = (const uint8_t*)(c.pk + (l2 ? P.conv2_s : P.conv3_s));
         a.ldo = cp;
         a.n_store = cp;
-        a.out_scale = (uint8_t*)(c.ws + (l2 ? W.a2_s : W.a3_s));
+        a.out_scale = (uint8_t*)(c.ws + (l2 ? W.a2_s : W.a3_s + a3_first * (cp / 32)));
         a.out_scale_rowmajor = 1;
         const double bytes = ((double)n * a.hin * a.win + (double)a.M) * cp * (1.0 + 1.0 / 32) +
                              (double)g.C * a.K * (1.0 + 1.0 / 32);
@@ -789,47 +834,16 @@ aut_status run_frontend(const Ctx& c, const float* feat, int T_max, float* hidde
       }
       if (st != AUT_OK) return st;
     }
-    // conv_out + positions over the batch's valid tokens
-    const int r0 = p.chunks[c0].row0;
-    const int r1 = (c0 + n < nch) ? p.chunks[c0 + n].row0 : (int)p.total;
-    if (r1 > r0) {
-      aut::GemmArgs a;
-      memset(&a, 0, sizeof(a));
-      a.A = c.ws + W.a3;
-      a.B = c.pk + P.conv_out_w;
-      a.M = r1 - r0;
-      a.N = g.d;
-      a.rowmap = d_rowmap + r0;
-      a.rowmap_base = c0 * g.w3;
-      a.tpc = g.w3;
-      a.bias = p.cfg.conv_out_bias ? pk_at<float>(c, P.conv_out_b) : nullptr;
-      a.out = hidden + (size_t)r0 * g.d;
-      a.ldo = g.d;
-      a.pe = pk_at<float>(c, P.pe);
-      aut_status st;
-      if (f8) {
-        a.lda = (long)g.h3 * cp;
-        a.ldb = (long)g.h3 * cp;
-        a.K = g.h3 * cp;
-        a.a_bytes = (size_t)n * g.w3 * g.h3 * cp;
-        a.a_scale = (const uint8_t*)(c.ws + W.a3_s);
-        a.a_scale_ld = g.h3 * cp / 32;
-        a.a_scale_bytes = (size_t)n * g.w3 * g.h3 * (cp / 32);
-        a.b_scale = (const uint8_t*)(c.pk + P.conv_out_s);
-        const double bytes = ((double)a.M * a.K + (double)g.d * a.K) * (1.0 + 1.0 / 32) +
-                             (double)a.M * g.d * 4;
-        st = gemm_f8(c, AUT_K_CONV_OUT, a, aut::A_ROWMAP, aut::EPI_PE, bytes);
-      } else {
-        a.lda = (long)g.h3 * g.C;
-        a.ldb = (long)g.h3 * g.C;
-        a.K = g.h3 * g.C;
-        a.a_bytes = (size_t)n * g.w3 * g.h3 * g.C * es;
-        const double bytes = ((double)a.M * a.K + (double)g.d * a.K) * es + (double)a.M * g.d * 4;
-        st = gemm(c, AUT_K_CONV_OUT, a, aut::A_ROWMAP, aut::EPI_PE, bytes);
-      }
+    // conv_out + positions over the batch's valid tokens (here only when a3
+    // holds one batch; otherwise once over all tokens below)
+    if (!W.a3_all) {
+      const int r0 = p.chunks[c0].row0;
+      const int r1 = (c0 + n < nch) ? p.chunks[c0 + n].row0 : (int)p.total;
+      const aut_status st = conv_out(r0, r1, c0, n);
       if (st != AUT_OK) return st;
     }
   }
+  if (W.a3_all && p.total > 0) return conv_out(0, (int)p.total, 0, nch);
   return AUT_OK;
 }
 
