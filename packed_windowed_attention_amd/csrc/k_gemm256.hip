@@ -315,6 +315,106 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& p, int m0, int n
   }
 }
 
+// Epilogue of a 288-row tile (two groups of nine 16-row blocks): passes of 96
+// rows, three blocks from each group, staged in six 16-row slots (slots 0-1 in
+// lds0, 2-3 in lds1, 4 in lds2, 5 in lds3: a 32-row fp32 slot pair needs
+// 33 KB, a single slot 17 KB), then copied out as in staged_epilogue.
+template <int BN, int WN, int NT, int EPI>
+__device__ __forceinline__ void staged_epilogue_288(const GemmArgs& p, int m0, int n0, int wm, int wn,
+                                                    int tid, f32x4_t (&acc)[WN / 16][9],
+                                                    u32x4_t* lds0, u32x4_t* lds1, u32x4_t* lds2,
+                                                    u32x4_t* lds3) {
+  constexpr int NTW = WN / 16;
+  static_assert(EPI == EPI_STORE || EPI == EPI_STORE_GELU || EPI == EPI_RESID || EPI == EPI_STORE_F32,
+                "288-row tiles: plain epilogues only");
+  constexpr bool F32 = EPI == EPI_RESID || EPI == EPI_STORE_F32;
+  constexpr int ES = F32 ? 4 : 2;
+  constexpr int RW = 144;                  // rows per group
+  constexpr int PR = 96;                   // rows per pass
+  constexpr int PITCH = BN * ES + 16;
+  constexpr int CPR = BN * ES / 16;
+  constexpr int EPC = 16 / ES;
+  constexpr int PER_THREAD = PR * CPR / NT;
+  static_assert(PR * CPR % NT == 0, "whole chunks per thread");
+  static_assert(32 * PITCH <= 256 * KU * 16 * 9 / 8 && 16 * PITCH <= BN * KU * 16, "slots fit the stages");
+  const int M = p.M, N = p.N;
+  const int lane = tid & 63, lrow = lane & 15, g = lane >> 4;
+  auto slot_base = [&](int slot) __attribute__((always_inline)) -> char* {
+    return slot < 2 ? (char*)lds0 + slot * 16 * PITCH
+         : slot < 4 ? (char*)lds1 + (slot - 2) * 16 * PITCH
+         : slot == 4 ? (char*)lds2 : (char*)lds3;
+  };
+  float4 bq[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int n = n0 + wn * WN + 16 * j + 4 * g;
+    bq[j] = (p.bias && n < N) ? *reinterpret_cast<const float4*>(p.bias + n)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  // bias in registers before any store (memory operations complete in issue order)
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) asm volatile("" ::"v"(bq[j].x), "v"(bq[j].y), "v"(bq[j].z), "v"(bq[j].w));
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    lds_barrier();
+#pragma unroll
+    for (int i = 3 * pass; i < 3 * pass + 3; ++i) {
+      char* base = slot_base(wm * 3 + (i - 3 * pass)) + lrow * PITCH;
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        f32x4_t av = acc[j][i];
+        asm volatile("" : "+v"(av));
+        float v[4] = {av[0] + bq[j].x, av[1] + bq[j].y, av[2] + bq[j].z, av[3] + bq[j].w};
+        if (EPI == EPI_STORE_GELU) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = gelu_bf16(v[r]);
+        }
+        const int col = wn * WN + 16 * j + 4 * g;
+        if (F32) {
+          *reinterpret_cast<f32x4_t*>(base + col * 4) = f32x4_t{v[0], v[1], v[2], v[3]};
+        } else {
+          *reinterpret_cast<u32x2_t*>(base + col * 2) =
+              u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+      }
+    }
+    lds_barrier();
+    constexpr int SB = PER_THREAD % 2 == 0 ? PER_THREAD / 2 : PER_THREAD;
+#pragma unroll
+    for (int s0 = 0; s0 < PER_THREAD; s0 += SB) {
+      u32x4_t d[SB];
+      float4 add[SB];
+      size_t off[SB];
+      bool ok[SB];
+#pragma unroll
+      for (int t = 0; t < SB; ++t) {
+        const int q = tid + NT * (s0 + t);
+        const int r = q / CPR;
+        const int c = q - r * CPR;
+        const int slot = r >> 4;
+        const int m = m0 + (slot / 3) * RW + pass * 48 + (slot % 3) * 16 + (r & 15);
+        const int n = n0 + c * EPC;
+        ok[t] = m < M && n < N;
+        d[t] = *reinterpret_cast<const u32x4_t*>(slot_base(slot) + (r & 15) * PITCH + c * 16);
+        off[t] = (size_t)m * p.ldo + n;
+        add[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (EPI == EPI_RESID && ok[t]) add[t] = *reinterpret_cast<const float4*>((const float*)p.out + off[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < SB; ++t) {
+        if (!ok[t]) continue;
+        if (!F32) {
+          *reinterpret_cast<u32x4_t*>((bf16_t*)p.out + off[t]) = d[t];
+        } else {
+          const f32x4_t f = __builtin_bit_cast(f32x4_t, d[t]);
+          *reinterpret_cast<float4*>((float*)p.out + off[t]) =
+              make_float4(f[0] + add[t].x, f[1] + add[t].y, f[2] + add[t].z, f[3] + add[t].w);
+        }
+      }
+    }
+  }
+}
+
 template <int BN> struct Stages { static constexpr int value = BN > 160 ? 2 : 3; };
 
 template <int BN, int AMODE, int EPI>
@@ -503,20 +603,30 @@ void gemm256_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
 
 // Eight-wave variant for wide column tiles (BN = 256 or 320): 8 waves (2 per
 // SIMD) in a 2 x 4 grid, each wave 128 x BN/4 (128 or 160 accumulators), two
-// LDS stages of 64 or 72 KiB.  Fewer operand bytes per flop than the
+// LDS stages of 64 or 72 KiB.  A 288 x 256 form (each wave 144 x 64, 144
+// accumulators, stages of 68 KiB) fits the 256 CUs' rounds better for some
+// row counts (14 673 rows: 51 tiles of 288 against 58 of 256).  Fewer operand bytes per flop than the
 // four-wave kernel (a 256 x 320 tile needs 7.0 bytes per k step per 1000
 // flops against 10.2 for 256 x 160).  With both waves of a SIMD reading,
 // loading and multiplying in step, the matrix cores were busy about half the
 // cycles; the ping-pong schedule below offsets the two rows of waves.
-template <int BN, int AMODE, int EPI>
+template <int BN, int AMODE, int EPI, int BMT = BM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
+  static_assert(BMT == BM || (BMT == 288 && AMODE == A_PLAIN && BN == 256),
+                "288-row tiles: plain A operand, 256 columns");
   constexpr int NT8 = 512;
   constexpr int WN = BN / 4;                 // columns per wave
   constexpr int NTW = WN / 16;               // 16-column tiles per wave
-  constexpr int A_UNITS = BM * KU;           // 2048 units per stage
+  constexpr int RW = BMT / 2;                // rows per wave (128 or 144)
+  constexpr int MB = RW / 16;                // 16-row blocks per wave (8 or 9)
+  constexpr int A_UNITS = BMT * KU;          // 2048 or 2304 units per stage
   constexpr int B_UNITS = BN * KU;
-  constexpr int A_LOADS = A_UNITS / NT8;     // 4 loads per thread per step
+  constexpr int A_LOADS = (A_UNITS + NT8 - 1) / NT8;  // 4 (or 5 on half the waves)
+  // the gathered modes (256-row tiles only) keep their per-load tables at a
+  // fixed size: tables sized by the row count made the host compilation pass
+  // drop the kernels' launch stubs without a diagnostic
+  constexpr int G_LOADS = BM * KU / NT8;
   constexpr int B_LOADS = B_UNITS / NT8;     // 4 or 5
   static_assert(B_UNITS % NT8 == 0, "whole B loads per thread");
   __shared__ u32x4_t As0[A_UNITS], As1[A_UNITS];
@@ -529,7 +639,7 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   const int first_m = group * GROUP_M;
   const int gsize = min(nM - first_m, GROUP_M);
   const int in_g = tile - group * per_group;
-  const int m0 = (first_m + in_g % gsize) * BM;
+  const int m0 = (first_m + in_g % gsize) * BMT;
   const int n0 = (in_g / gsize) * BN;
 
   const int tid = threadIdx.x;
@@ -553,11 +663,11 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   }
   const unsigned a_step = (unsigned)(64 * p.lda * 2);
   const unsigned a_off0 = (unsigned)((wave * 8 + lrow8) * p.lda * 2);
-  unsigned a_rowoff[A_LOADS];
-  ConvGather<A_LOADS, 2> cg;  // (full size in every mode: see ConvGather)
+  unsigned a_rowoff[G_LOADS];
+  ConvGather<G_LOADS, 2> cg;  // (full size in every mode: see ConvGather)
   if (AMODE != A_PLAIN) {
 #pragma unroll
-    for (int j = 0; j < A_LOADS; ++j) {
+    for (int j = 0; j < G_LOADS; ++j) {
       const int m = m0 + (j * 8 + wave) * 8 + lrow8;
       if (AMODE == A_ROWMAP) {
         a_rowoff[j] = m < M ? (unsigned)((size_t)(p.rowmap[m] - p.rowmap_base) * p.lda * 2) : OOB;
@@ -582,18 +692,22 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
     if (AMODE == A_CONV) {
       const int toff = cg.tap_offset(p);
 #pragma unroll
-      for (int j = 0; j < A_LOADS; ++j)
+      for (int j = 0; j < G_LOADS; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(j * 8 + wave) * 64]), 16,
                                                  cg.offset(j, toff), 0, 0, 0);
       cg.advance(BK, p.cin);  // steps are issued in increasing order
-    } else {
+    } else if (AMODE == A_PLAIN) {
 #pragma unroll
       for (int j = 0; j < A_LOADS; ++j) {
-        const unsigned off = AMODE == A_PLAIN ? a_off0 + j * a_step + koff
-                                              : (a_rowoff[j] == OOB ? OOB : a_rowoff[j] + koff);
+        if (A_UNITS % NT8 != 0 && (j * 8 + wave) * 64 >= A_UNITS) continue;  // uniform per wave
         __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(j * 8 + wave) * 64]), 16,
-                                                 off, 0, 0, 0);
+                                                 a_off0 + j * a_step + koff, 0, 0, 0);
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < G_LOADS; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dma_dst(&As_s[(j * 8 + wave) * 64]), 16,
+                                                 a_rowoff[j] == OOB ? OOB : a_rowoff[j] + koff, 0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < B_LOADS; ++j)
@@ -601,11 +715,11 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
                                                b_off0 + j * b_step + koff, 0, 0, 0);
   };
 
-  f32x4_t acc[NTW][8];
+  f32x4_t acc[NTW][MB];
 #pragma unroll
   for (int j = 0; j < NTW; ++j)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < MB; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (K + BK - 1) / BK;
   const int lrow = lane & 15;
@@ -622,7 +736,7 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
   // phase 3 of step kt - 1, after every wave has finished reading step kt - 1
   // there (the readers wait for their reads before the barrier that precedes
   // a refill).  Each output still sums its k steps in increasing order.
-  FragBF16 xa[8], wb[NTW];
+  FragBF16 xa[MB], wb[NTW];
   auto rd = [&](const u32x4_t* As_s, const u32x4_t* Bs_s, int h) __attribute__((always_inline)) {
     const int u = 4 * h + g;
 #pragma unroll
@@ -631,15 +745,15 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
       frag_from_units(wb[j], Bs_s[r * KU + swz(u, r)], zero_unit());
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = wm * 128 + 16 * i + lrow;
+    for (int i = 0; i < MB; ++i) {
+      const int r = wm * RW + 16 * i + lrow;
       frag_from_units(xa[i], As_s[r * KU + swz(u, r)], zero_unit());
     }
   };
   auto mm = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < NTW; ++j) mma16_k32(acc[j][i], wb[j], xa[i]);
     __builtin_amdgcn_s_setprio(0);
@@ -704,7 +818,10 @@ void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
       if (kt + 1 < nk) g1step(kt + 1, As1, Bs1, As0, Bs0);
     }
   }
-  staged_epilogue<BN, WN, NT8, EPI>(p, m0, n0, wm, wn, tid, acc, As0, As1, Bs0, Bs1);
+  if constexpr (BMT == BM)
+    staged_epilogue<BN, WN, NT8, EPI>(p, m0, n0, wm, wn, tid, acc, As0, As1, Bs0, Bs1);
+  else
+    staged_epilogue_288<BN, WN, NT8, EPI>(p, m0, n0, wm, wn, tid, acc, As0, As1, Bs0, Bs1);
 }
 
 // MX-fp8 variant of the eight-wave kernel (OCP Microscaling MX-fp8 operands:
@@ -1077,13 +1194,13 @@ hipError_t run8_f8(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BN, int AMODE, int EPI>
+template <int BN, int AMODE, int EPI, int BMT = BM>
 hipError_t run8(const GemmArgs& a, hipStream_t s) {
-  const int nM = (a.M + BM - 1) / BM;
+  const int nM = (a.M + BMT - 1) / BMT;
   const int nN = (a.N + BN - 1) / BN;
   const int tiles = nM * nN;
   const int per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL((gemm8w_kernel<BN, AMODE, EPI>), dim3(8 * per_xcd), dim3(512), 0, s, a, nM,
+  hipLaunchKernelGGL((gemm8w_kernel<BN, AMODE, EPI, BMT>), dim3(8 * per_xcd), dim3(512), 0, s, a, nM,
                      nN, per_xcd);
   return hipGetLastError();
 }
@@ -1124,6 +1241,21 @@ hipError_t dispatch(const GemmArgs& a, int amode, int epi, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// 288 x 256 tiles of the eight-wave kernel (plain A operand and the plain
+// epilogues only)
+hipError_t dispatch288(const GemmArgs& a, int amode, int epi, hipStream_t s) {
+  if (amode == A_PLAIN) {
+    switch (epi) {
+      case EPI_STORE: return run8<256, A_PLAIN, EPI_STORE, 288>(a, s);
+      case EPI_STORE_GELU: return run8<256, A_PLAIN, EPI_STORE_GELU, 288>(a, s);
+      case EPI_RESID: return run8<256, A_PLAIN, EPI_RESID, 288>(a, s);
+      case EPI_STORE_F32: return run8<256, A_PLAIN, EPI_STORE_F32, 288>(a, s);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
 // Column tile for an N: the candidate with the best estimated throughput,
 // i.e. tile-slot use on 256 CUs (partly empty last round, columns past N)
 // times the measured relative speed of the kernel per tile-slot (eight-wave
@@ -1148,6 +1280,25 @@ int pick_bn(int M, int N) {
     }
   }
   return best;
+}
+
+// Whether a 288 x 256 tile beats the eight-wave column tile pick_bn chose:
+// estimated time = rounds of 256 tiles x (k steps x per-step cost + per-tile
+// cost), with the costs measured on MI355X on the layer GEMM shapes (us with
+// every CU busy: 256 x 320 1.65 per 64-deep step and ~20 per tile, 288 x 256
+// 1.69 and ~18.5, 256 x 256 1.49 and ~18).  It wins where the k loop is short
+// against the epilogue and the row count fits 288-row tiles better (14 673
+// rows at K = 1280: 51 tiles of 288 against 58 of 256), and loses on long k
+// loops (K = 5120).
+bool use_288(int M, int N, int K, int bn) {
+  if (bn != 320 && bn != 256) return false;
+  const long nk = (K + BK - 1) / BK;
+  auto est = [&](int bm, int bnn, double step, double tile) {
+    const long tiles = (long)((M + bm - 1) / bm) * ((N + bnn - 1) / bnn);
+    return (double)((tiles + 255) / 256) * ((double)nk * step + tile);
+  };
+  const double cur = bn == 320 ? est(256, 320, 1.65, 20.0) : est(256, 256, 1.49, 18.0);
+  return est(288, 256, 1.69, 18.5) < cur * (1.0 - 1e-9);
 }
 
 // the epilogue copies 16-byte chunks (or, for MX output, 32-value blocks) of
@@ -1231,7 +1382,13 @@ hipError_t launch_gemm256(const GemmArgs& a, int amode, int epi, hipStream_t s) 
   if (!epilogue_fits(a, epi)) return hipErrorInvalidValue;
   // gathered A: one descriptor over the whole buffer, 32-bit offsets below OOB
   if (amode != A_PLAIN && a.a_bytes >= (size_t)OOB) return hipErrorInvalidValue;
+  // 288-row tiles: plain A operand, plain epilogues (a tuning value of 288
+  // forces them)
+  const bool plain = amode == A_PLAIN && (epi == EPI_STORE || epi == EPI_STORE_GELU ||
+                                          epi == EPI_RESID || epi == EPI_STORE_F32);
   const int bn = g_gemm256_force_bn ? g_gemm256_force_bn : pick_bn(a.M, a.N);
+  if (bn == 288 || (!g_gemm256_force_bn && plain && use_288(a.M, a.N, a.K, bn)))
+    return plain ? dispatch288(a, amode, epi, s) : hipErrorInvalidValue;
   switch (bn) {
     case 320: return dispatch<320>(a, amode, epi, s);
     case 256: return dispatch<256>(a, amode, epi, s);
