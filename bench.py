@@ -35,7 +35,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_wide_hbm_traffic.md")
 GEMM_SOURCES = ("packed_windowed_attention_amd/csrc/k_gemm256.hip",
                 "packed_windowed_attention_amd/csrc/device_common.h",
                 "packed_windowed_attention_amd/csrc/aut_internal.h")
-LAYER_GEMM_RE = r"gemm(8w|256)_kernel<\d+, 0, \d+>"
+LAYER_GEMM_RE = r"gemm(8w|256)_kernel<\d+, 0, \d+(, \d+)?>"
 
 METRIC = "encoder tokens/s and audio-sec/s on 1 MI355X; % of bf16 MFMA peak"
 
