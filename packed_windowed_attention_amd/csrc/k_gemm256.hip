@@ -605,11 +605,12 @@ void gemm256_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
 // SIMD) in a 2 x 4 grid, each wave 128 x BN/4 (128 or 160 accumulators), two
 // LDS stages of 64 or 72 KiB.  A 288 x 256 form (each wave 144 x 64, 144
 // accumulators, stages of 68 KiB) fits the 256 CUs' rounds better for some
-// row counts (14 673 rows: 51 tiles of 288 against 58 of 256).  Fewer operand bytes per flop than the
-// four-wave kernel (a 256 x 320 tile needs 7.0 bytes per k step per 1000
-// flops against 10.2 for 256 x 160).  With both waves of a SIMD reading,
-// loading and multiplying in step, the matrix cores were busy about half the
-// cycles; the ping-pong schedule below offsets the two rows of waves.
+// row counts (14 673 rows: 51 tiles of 288 against 58 of 256).  Fewer operand
+// bytes per flop than the four-wave kernel (a 256 x 320 tile needs 7.0 bytes
+// per k step per 1000 flops against 10.2 for 256 x 160).  With both waves of a
+// SIMD reading, loading and multiplying in step, the matrix cores were busy
+// about half the cycles; the ping-pong schedule below offsets the two rows of
+// waves.
 template <int BN, int AMODE, int EPI, int BMT = BM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm8w_kernel(GemmArgs p, int nM, int nN, int per_xcd) {
