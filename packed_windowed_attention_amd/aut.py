@@ -111,6 +111,12 @@ def lib():
         if not os.path.exists(LIB_PATH):
             from . import build as _build
             _build.build()
+        # PyTorch ships its own HIP runtime under the same soname as the
+        # system one this library links: load it first, so that the process
+        # has one runtime.  (With the library loaded first, the system runtime
+        # came in beside PyTorch's own libraries, and every launch from the
+        # library failed with "no ROCm-capable device" while torch ran.)
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(L, name)

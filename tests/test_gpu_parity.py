@@ -290,6 +290,25 @@ def test_window_isolation_bitwise():
     assert dev == 0.0
 
 
+def test_batch_composition_bitwise():
+    """A request's output rows do not depend on what else is in the batch, bit
+    for bit: the wide batch (14 673 rows; its layer GEMMs run 288 x 256 and
+    256 x 320 tiles, its conv GEMMs 256 x 256) against three of its requests
+    encoded alone (a few hundred rows; narrower tiles). Every GEMM output sums
+    its k steps in the same order in every tile shape, and every other step
+    works per row or per window (m-star module summary: attention stays
+    inside each window)."""
+    cfg_d, lens, feats, P = workload("wide")
+    cfg, packed = pack(cfg_d, P)
+    y, pl = forward(cfg_d, lens, feats, packed=packed, cfg=cfg)
+    off = np.concatenate([[0], np.cumsum(pl.copy()[0])])
+    for b in (0, len(lens) // 2, len(lens) - 1):
+        print(f"case: request {b} alone ({off[b + 1] - off[b]} rows) against the wide batch", flush=True)
+        yb, _ = forward(cfg_d, lens[b:b + 1], feats[b:b + 1], packed=packed, cfg=cfg)
+        assert yb.shape == (off[b + 1] - off[b], y.shape[1])
+        assert np.array_equal(yb, y[off[b]:off[b + 1]]), b
+
+
 def test_run_twice_bitwise():
     """Full-width workload twice: identical bits (no order-dependent reductions)."""
     cfg_d, lens, feats, P = workload("wide")
