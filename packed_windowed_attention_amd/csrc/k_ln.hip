@@ -17,10 +17,27 @@ constexpr int LN_WAVES = 4;
 constexpr int LN_MAXV = 8;            // float4 per lane: d <= 2048
 constexpr int LN_GRID_CAP = 256 * 4;  // workgroups: 16 waves per CU, each over several rows
 
-// butterfly sum over the wavefront
+// Sum over the wavefront, the same value in every lane, without LDS: lane
+// pairs and quad pairs by DPP quad permutes, then the 4-lane halves of each
+// 8-lane group and the 8-lane halves of each 16-lane row by DPP mirrors (on
+// values already uniform over the quads or halves these are the xor-4 and
+// xor-8 partners), then row pairs and row halves by v_permlane16_swap and
+// v_permlane32_swap.  Each step adds two partners' values, so every lane adds
+// the same pairs and ends with the same bits.
 __device__ __forceinline__ void wave_sum_n(float (&v)[1]) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v[0] += __shfl_xor(v[0], o, 64);
+  float x = v[0];
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                          1 | (0 << 2) | (3 << 4) | (2 << 6), 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                          2 | (3 << 2) | (0 << 4) | (1 << 6), 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF,
+                                                          false));  // row_half_mirror
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF,
+                                                          false));  // row_mirror
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  v[0] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // four consecutive outputs in one store (8 bytes bf16, 16 bytes fp32)
