@@ -113,8 +113,8 @@ __device__ __forceinline__ void store_row_mx(uint8_t* orow, uint8_t* osc, int ro
     for (int dt = 2 * blk; dt < 2 * blk + 2; ++dt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(v[dt][r]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    amax = pair_max16(amax);
+    amax = pair_max32(amax);
     if (!live) continue;
     const int e = mx_exponent(amax);
 #pragma unroll

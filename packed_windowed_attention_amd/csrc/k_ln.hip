@@ -54,9 +54,13 @@ __device__ __forceinline__ void store_row4(float* p, float a, float b, float c, 
 __device__ __forceinline__ void store_row4_mx(uint8_t* yr, uint8_t* sc, int row, int c, int d,
                                               float a, float b, float e, float f, bool live) {
   float amax = fmaxf(fmaxf(fabsf(a), fabsf(b)), fmaxf(fabsf(e), fabsf(f)));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+  // the 8 lanes of an aligned group: quad permutes, then the group's half mirror
+  amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                         __builtin_bit_cast(int, amax), 1 | (0 << 2) | (3 << 4) | (2 << 6), 0xF, 0xF, false)));
+  amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                         __builtin_bit_cast(int, amax), 2 | (3 << 2) | (0 << 4) | (1 << 6), 0xF, 0xF, false)));
+  amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                         __builtin_bit_cast(int, amax), 0x141, 0xF, 0xF, false)));  // row_half_mirror
   if (!live) return;
   const int x = mx_exponent(amax);
   *reinterpret_cast<unsigned int*>(yr + 4 * c) =
