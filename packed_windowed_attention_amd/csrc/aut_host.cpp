@@ -531,6 +531,33 @@ struct WsLayout {
   int nb;  // chunks per conv-stem batch
 };
 
+// Chunks per conv-stem batch, at most cap.  A conv GEMM's grid runs in
+// rounds of one tile per CU, so a batch whose tile count just passes a
+// multiple of the CU count pays a nearly empty last round.  Among batch sizes
+// from cap down to cap / 2, at most 512 of them (batches of that size, the
+// rest in a last one), this
+// takes the one with the least estimated conv2 + conv3 time, ties to the
+// larger size.  Results do not depend on it: every output pixel sums its k
+// steps in the same order in any batch.
+int conv_batch_chunks(int nch, int cap, const Geometry& g, bool f8) {
+  if (nch <= 0 || cap <= 1) return cap;
+  auto t = [&](int n) {
+    return aut::gemm_conv_time_model(n * g.h2 * g.w2, g.C, f8) +
+           aut::gemm_conv_time_model(n * g.h3 * g.w3, g.C, f8);
+  };
+  int best = cap;
+  double best_t = 0.0;
+  for (int n = cap; n >= std::max(std::max(1, cap / 2), cap - 511); --n) {
+    const int full = nch / n, rest = nch - full * n;
+    const double tn = full * t(n) + (rest ? t(rest) : 0.0);
+    if (n == cap || tn < best_t * (1.0 - 1e-9)) {
+      best = n;
+      best_t = tn;
+    }
+  }
+  return best;
+}
+
 WsLayout ws_layout(const aut_plan_t& p, aut_dtype dt) {
   const Geometry& g = p.geo;
   WsLayout W;
@@ -552,6 +579,7 @@ WsLayout ws_layout(const aut_plan_t& p, aut_dtype dt) {
   const size_t per_chunk = (size_t)g.h1 * g.w1 * cs;
   const size_t max_nb = std::max<size_t>(1, ((size_t)1 << 31) / per_chunk - 1);
   W.nb = (int)std::min<size_t>(std::min<size_t>((size_t)p.cfg.conv_chunksize, nch), max_nb);
+  if (dt != AUT_FP32) W.nb = conv_batch_chunks((int)nch, W.nb, g, f8c);
   const size_t nb = (size_t)W.nb;
   W.chunks = take(nch * sizeof(aut_chunk));
   W.rowmap = take(T * 4);

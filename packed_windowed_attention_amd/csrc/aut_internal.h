@@ -117,6 +117,9 @@ hipError_t launch_gemm256(const GemmArgs& a, int amode, int epi, hipStream_t s);
 // EPI_STORE, EPI_STORE_GELU, EPI_RESID, EPI_STORE_F32, EPI_GELU_MX; A_CONV
 // with EPI_GELU_MX; A_ROWMAP with EPI_PE.
 hipError_t launch_gemm_f8(const GemmArgs& a, int amode, int epi, hipStream_t s);
+// relative duration of an implicit-conv GEMM launch (M output pixels, N
+// channels) under the tile choice the launchers make (bf16 or MX-fp8 kernel)
+double gemm_conv_time_model(int M, int N, bool f8);
 
 // conv-stem weights straight from their PyTorch layout to MX-fp8, channels
 // padded to cp with zeros: mode PACK_CONV, [Co, Ci, 3, 3] -> [Co][tap * cp + c];

@@ -1362,6 +1362,19 @@ int pick_bn_f8(int M, int N) {
 
 int g_gemm_f8_force_bn = 0;  // tuning hook: 0 = automatic
 
+// Relative duration of a gathered-A (conv) launch of M x N in the model the
+// column-tile choice uses: rounds of 256 tiles (one tile per CU at a time,
+// every tile of a launch equally long) times a tile's width over the kernel's
+// relative speed per tile slot.  K drops out (the conv GEMMs share it).
+double gemm_conv_time_model(int M, int N, bool f8) {
+  if (M <= 0 || N <= 0) return 0.0;
+  const int bn = f8 ? (g_gemm_f8_force_bn ? g_gemm_f8_force_bn : pick_bn_f8(M, N))
+                    : (g_gemm256_force_bn ? g_gemm256_force_bn : pick_bn(M, N));
+  const long tiles = (long)((M + BM - 1) / BM) * ((N + bn - 1) / bn);
+  const double speed = f8 ? 1.0 : (bn >= 256 ? 1.3 : bn == 160 ? 1.0 : 0.87);
+  return (double)((tiles + 255) / 256) * (double)bn / speed;
+}
+
 hipError_t launch_gemm_f8(const GemmArgs& a, int amode, int epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K <= 0 || a.K % 128 || a.lda % 16 || a.ldb % 16 || !a.a_scale || !a.b_scale ||

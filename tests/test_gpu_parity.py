@@ -309,6 +309,23 @@ def test_batch_composition_bitwise():
         assert np.array_equal(yb, y[off[b]:off[b + 1]]), b
 
 
+@pytest.mark.parametrize("dtype,mask", [("bf16", 0), ("fp8", 32)])
+def test_conv_batch_size_bitwise(dtype, mask):
+    """conv_chunksize only sets how many chunks one conv-stem launch takes
+    (memory), and the library picks batch sizes below it that fill the conv
+    GEMMs' rounds of tiles: the wide workload's whole output is bit-identical
+    whether the stem runs in two batches (~700 chunks) or in thirteen (<= 97)."""
+    cfg_d, lens, feats, P = workload("wide")
+    cfg_d = dict(cfg_d, dtype=dtype, fp8_gemms=mask)
+    ys = []
+    for cs in (4096, 97):
+        print(f"case: wide {dtype} mask {mask}, conv_chunksize {cs}", flush=True)
+        y, _ = forward(dict(cfg_d, conv_chunksize=cs), lens, feats, P)
+        ys.append(y)
+    assert np.isfinite(ys[0]).all()
+    assert np.array_equal(ys[0], ys[1])
+
+
 def test_run_twice_bitwise():
     """Full-width workload twice: identical bits (no order-dependent reductions)."""
     cfg_d, lens, feats, P = workload("wide")
