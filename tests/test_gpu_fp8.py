@@ -166,6 +166,31 @@ def test_rag_fp8():
     check_fp8(y, ref_q, ref, "rag fp8")
 
 
+@pytest.mark.parametrize("name", ["conc"])
+def test_page_mask_other_workloads(name):
+    """The conv stem on MX-fp8 (PAGE_MASK) on the high-concurrency workload
+    (512 log-normal requests: many partial chunks and short tail windows), at
+    least 8 sampled windows: within the quantisation noise bound of the fp8
+    oracle, and every token's cosine to the unquantised encoder above the
+    pages' 0.999 (the oracle's model of the format gives min 0.99991 on these
+    windows)."""
+    cfg_d, lens, feats, P = workload(name)
+    cfg_d = dict(cfg_d, dtype="fp8", fp8_gemms=PAGE_MASK)
+    print(f"case: {name} fp8 mask {PAGE_MASK}, sampled windows", flush=True)
+    y, pl = forward(cfg_d, lens, feats, P)
+    opl = oracle.plan(lens, cfg_d)
+    assert pl.copy()[1] == opl["cu_seqlens"]
+    wins = sample_windows(opl, seed=si.workload_seed(name) + 3)
+    assert len(wins) >= 8, wins
+    res_q = oracle.forward_windows(feats, lens, P, cfg_d, wins, fp8=PAGE_MASK)
+    res = oracle.forward_windows(feats, lens, P, cfg_d, wins)
+    cos = np.concatenate([check_fp8(y[res_q[w][0]:res_q[w][0] + res_q[w][1].shape[0]], res_q[w][1], res[w][1],
+                                    f"{name} mask {PAGE_MASK} window {w}") for w in wins])
+    print(f"[{name} mask {PAGE_MASK}] vs unquantized over windows {wins}: min cos {cos.min():.6f} "
+          f"mean {cos.mean():.6f}", flush=True)
+    assert cos.min() > PAGE_COS
+
+
 @pytest.mark.parametrize("mask", [PAGE_MASK, 63, 1])
 def test_wide_fp8_sampled_windows(mask):
     """Full-width workload (24 layers, d 1280) under AUT_FP8, at least 8
