@@ -411,6 +411,39 @@ aut_status aut_layernorm(const float* x, int64_t rows, int32_t d, const float* g
                          const float* beta, float eps, aut_dtype dtype, void* y,
                          uint8_t* y_scales, void* stream);
 
+/* ------------------------------------------------------------------------
+ * One window-attention step on its own, with the kernel the forward uses:
+ * for every window [s, e) of cu_seqlens and every head h, softmax(Q K^T /
+ * sqrt(64)) V over the window's own rows only, bidirectional, with no mask
+ * inside the window and nothing across windows (m-star API page, module
+ * summary and AuTAttention: SDPA per window from cu_seqlens; openarchlab
+ * "1A", section 3: is_causal = False).  Head dimension 64, d = 64 heads.
+ *   qkv:          device [rows, 3 d] in in_dtype, row-major: q in columns
+ *                 [0, d), k in [d, 2d), v in [2d, 3d); head h owns columns
+ *                 [64 h, 64 h + 64) of each; 16-byte aligned
+ *   cu_seqlens:   device int32 [n_windows + 1], window w = rows
+ *                 [cu[w], cu[w + 1]), at most 128 rows each
+ *   window_order: device int32 [n_windows], a permutation of the windows:
+ *                 the order the kernel takes them in (longest first fills
+ *                 the machine best); results do not depend on it
+ *   in -> out:    AUT_FP32 -> AUT_FP32; AUT_BF16 -> AUT_BF16 (each value the
+ *                 fp32 result rounded to nearest even), AUT_FP32 (those fp32
+ *                 results) or AUT_FP8 (e4m3 codes [rows, d] and, in
+ *                 out_scales, aut_mx_scale_bytes(rows, d) scale bytes in the
+ *                 MX layout above, each 32-value block of a row quantised
+ *                 from the fp32 results as aut_mx_quantize would; heads
+ *                 even)
+ *   out:          device [rows, d] of out_dtype, 16-byte aligned
+ * Rows of no window are not written.  A window outside rows [0, rows), longer
+ * than 128 rows or named by an order entry outside [0, n_windows) is skipped
+ * (its rows are not written).  The caller owns every buffer.  Returns
+ * INVALID_ARG for NULL pointers, misalignment or negative counts,
+ * UNSUPPORTED for other dtype pairs or head counts.  Asynchronous on
+ * `stream`. */
+aut_status aut_attention(const void* qkv, int64_t rows, int32_t heads, const int32_t* cu_seqlens,
+                         const int32_t* window_order, int32_t n_windows, aut_dtype in_dtype,
+                         aut_dtype out_dtype, void* out, uint8_t* out_scales, void* stream);
+
 /* Kernel classes for the optional per-launch timing below. */
 typedef enum {
   AUT_K_CONV1 = 0,     /* conv1 (+GELU), fp32 vector ALU */

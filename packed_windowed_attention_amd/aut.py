@@ -94,6 +94,8 @@ SIGNATURES = {
                               c_void_p, c_void_p]),
     "aut_encode_noalloc": (c_int, [POINTER(AutConfig), c_void_p, c_int32, POINTER(c_int32), c_int32, c_void_p,
                                     c_int, c_void_p, c_void_p]),
+    "aut_attention": (c_int, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_int32, c_int, c_int,
+                              c_void_p, c_void_p, c_void_p]),
     "aut_layernorm": (c_int, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_float, c_int, c_void_p,
                                c_void_p, c_void_p]),
     "aut_profile_enable": (c_int, [c_int]),
@@ -508,6 +510,42 @@ def mx_matmul(a_codes, a_scales, b_codes, b_scales, out=None, stream=None):
     _check(lib().aut_mx_matmul(_ptr(a_codes), _ptr(a_scales), M, _ptr(b_codes), _ptr(b_scales), N,
                                K, _ptr(out), _stream_ptr(stream)))
     return out
+
+
+def attention(qkv, cu_seqlens, window_order, heads: int, out_dtype=None, stream=None):
+    """aut_attention: qkv [R, 3 d] (float32 or bfloat16, contiguous, on the
+    device) with device int32 cu_seqlens [n + 1] and window_order [n] ->
+    out [R, d] in out_dtype ("fp32", "bf16" or, from bf16 qkv, "fp8": e4m3
+    codes uint8 [R, d] and scale codes in the MX layout).  Default out_dtype:
+    qkv's.  Rows outside every window are returned as zero."""
+    import torch
+    if qkv.dim() != 2 or not qkv.is_contiguous() or qkv.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("qkv must be a contiguous 2-D float32 or bfloat16 tensor")
+    in_dt = "fp32" if qkv.dtype == torch.float32 else "bf16"
+    out_dtype = out_dtype or in_dt
+    R = qkv.shape[0]
+    d = 64 * int(heads)
+    if qkv.shape[1] != 3 * d:
+        raise ValueError(f"qkv has {qkv.shape[1]} columns, 3 x 64 x heads = {3 * d} expected")
+    for t in (cu_seqlens, window_order):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or t.device != qkv.device:
+            raise ValueError("cu_seqlens and window_order must be contiguous int32 vectors on qkv's device")
+    n = window_order.numel()
+    if cu_seqlens.numel() != n + 1:
+        raise ValueError("cu_seqlens must hold one more entry than window_order")
+    odt = _dtype(out_dtype)
+    scales = None
+    if odt == DTYPES["fp8"]:
+        out = torch.zeros((R, d), dtype=torch.uint8, device=qkv.device)
+        nsc = mx_scale_bytes(R, d) if d % 128 == 0 else 1
+        scales = torch.zeros(max(1, nsc), dtype=torch.uint8, device=qkv.device)
+    else:
+        out = torch.zeros((R, d), dtype=torch.float32 if odt == DTYPES["fp32"] else torch.bfloat16,
+                          device=qkv.device)
+    _check(lib().aut_attention(_ptr(qkv), R, int(heads), _ptr(cu_seqlens), _ptr(window_order), n,
+                               _dtype(in_dt), odt, _ptr(out), _ptr(scales) if scales is not None else None,
+                               _stream_ptr(stream)))
+    return (out, scales) if scales is not None else out
 
 
 def layernorm(x, gamma, beta, dtype="fp32", eps=1e-5, stream=None):

@@ -936,7 +936,7 @@ aut_status run_encode(const Ctx& c, float* out) {
     aut::prof_begin(c.s);
     hipError_t e = aut::launch_attention(qkv, o, (const int*)(c.ws + W.cu),
                                          (const int*)(c.ws + W.worder), (int)p.cu.size() - 1, g.H,
-                                         d, f_out ? AUT_FP8 : c.dt, c.s, f_out ? o_s : nullptr);
+                                         d, f_out ? AUT_FP8 : c.dt, c.s, f_out ? o_s : nullptr, T);
     if (e != hipSuccess) return fail(AUT_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
     aut::prof_end(c.s, AUT_K_ATTENTION, 4.0 * d * p.sum_len2, 3.0 * T * d * es + T * d * (f_out ? e8 : es));
     st = prod(f_out, plain_args(o, c.pk + l.o_w, T, d, d, pk_at<float>(c, l.o_b), x, d), o_s, l.o_s,
@@ -1347,6 +1347,36 @@ extern "C" aut_status aut_layernorm(const float* x, int64_t rows, int32_t d, con
   hipError_t e = aut::launch_layernorm(x, gamma, beta, y, (int)rows, d, eps, dtype, (hipStream_t)stream,
                                        y_scales);
   if (e != hipSuccess) return fail(AUT_ERR_HIP, "layernorm launch failed: %s", hipGetErrorString(e));
+  return AUT_OK;
+}
+
+extern "C" aut_status aut_attention(const void* qkv, int64_t rows, int32_t heads,
+                                    const int32_t* cu_seqlens, const int32_t* window_order,
+                                    int32_t n_windows, aut_dtype in_dtype, aut_dtype out_dtype,
+                                    void* out, uint8_t* out_scales, void* stream) {
+  if (rows < 0 || n_windows < 0)
+    return fail(AUT_ERR_INVALID_ARG, "rows = %lld and n_windows = %d must not be negative",
+                (long long)rows, n_windows);
+  const bool ok_pair = (in_dtype == AUT_FP32 && out_dtype == AUT_FP32) ||
+                       (in_dtype == AUT_BF16 && (out_dtype == AUT_BF16 || out_dtype == AUT_FP32 ||
+                                                 out_dtype == AUT_FP8));
+  if (!ok_pair)
+    return fail(AUT_ERR_UNSUPPORTED, "dtypes (%d -> %d): fp32 -> fp32, bf16 -> bf16, fp32 or fp8",
+                (int)in_dtype, (int)out_dtype);
+  if (heads <= 0 || heads > 64 || (out_dtype == AUT_FP8 && heads % 2))
+    return fail(AUT_ERR_UNSUPPORTED, "heads = %d: 1 to 64 (even for fp8 output)", heads);
+  if (rows >= ((int64_t)1 << 31)) return fail(AUT_ERR_UNSUPPORTED, "rows = %lld: at most 2^31 - 1", (long long)rows);
+  if (rows == 0 || n_windows == 0) return AUT_OK;
+  if (!qkv || !cu_seqlens || !window_order || !out || (out_dtype == AUT_FP8 && !out_scales))
+    return fail(AUT_ERR_INVALID_ARG, "NULL pointer");
+  if (((size_t)qkv & 15) || ((size_t)out & 15) || ((size_t)cu_seqlens & 3) || ((size_t)window_order & 3))
+    return fail(AUT_ERR_INVALID_ARG, "qkv and out must be 16-byte aligned, the tables 4-byte aligned");
+  const int d = 64 * heads;
+  const aut_dtype kdt = out_dtype == AUT_FP8 ? AUT_FP8 : in_dtype;
+  hipError_t e = aut::launch_attention(qkv, out, cu_seqlens, window_order, n_windows, heads, d, kdt,
+                                       (hipStream_t)stream, out_scales, (int)rows,
+                                       in_dtype == AUT_BF16 && out_dtype == AUT_FP32);
+  if (e != hipSuccess) return fail(AUT_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   return AUT_OK;
 }
 

@@ -138,10 +138,12 @@ hipError_t launch_mx_quantize(const float* x, long ldx, long R, int K, uint8_t* 
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, int T, int d,
                             float eps, aut_dtype dt, hipStream_t s, uint8_t* y_scales = nullptr);
 
-// Window attention: qkv [T, 3d] (q | k | v) -> o [T, d].  AUT_FP8: bf16 qkv,
-// o as MX-fp8 codes with scales in o_scales.
+// Window attention: qkv [T, 3d] (q | k | v) -> o [T, d], d = 64 H.  AUT_FP8:
+// bf16 qkv, o as MX-fp8 codes with scales in o_scales.  f32_out (AUT_BF16
+// only): o in fp32, the values the bf16 and MX outputs round.  Items whose
+// window is not within rows [0, T) or holds more than 128 rows do nothing.
 hipError_t launch_attention(const void* qkv, void* o, const int* cu, const int* worder,
                             int n_windows, int H, int d, aut_dtype dt, hipStream_t s,
-                            uint8_t* o_scales = nullptr);
+                            uint8_t* o_scales, int T, bool f32_out = false);
 
 }  // namespace aut

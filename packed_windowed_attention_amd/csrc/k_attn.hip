@@ -141,16 +141,23 @@ struct ItemRegs {
 
 struct Item {
   int s0, L, h;
+  bool ok;
 };
 
+// A window order entry outside [0, n_windows), or a window that is not within
+// rows [0, T) or holds more than LMAX rows, gives an item that does nothing
+// (the planner never makes one; the check keeps a caller's bad table from
+// reading or writing outside the buffers).
 __device__ __forceinline__ Item item_of(int item, const int* __restrict__ cu,
-                                        const int* __restrict__ worder, int H) {
+                                        const int* __restrict__ worder, int H, int n_windows, int T) {
   const int wi = item / H;
   const int w = worder[wi];
   Item it;
   it.h = item - wi * H;
-  it.s0 = cu[w];
-  it.L = cu[w + 1] - it.s0;
+  it.ok = w >= 0 && w < n_windows;
+  it.s0 = it.ok ? cu[w] : 0;
+  it.L = it.ok ? cu[w + 1] - it.s0 : 0;
+  it.ok = it.ok && it.s0 >= 0 && it.L >= 0 && it.L <= LMAX && it.s0 <= T - it.L;
   return it;
 }
 
@@ -243,7 +250,7 @@ __device__ __forceinline__ void stage_item(const ItemRegs<T>& r, u32x4_t* Ks, T*
 // every tile (MASK_ALL, short windows) or in the last one only.  A lane ends
 // up with one query's scores (its column of S^T), so the softmax reductions
 // are in-lane plus two wavefront shuffles.
-template <typename T, bool MX, int NKT, bool MASK_ALL>
+template <typename T, typename OT, bool MX, int NKT, bool MASK_ALL>
 __device__ __forceinline__ void query_tile(const u32x4_t* Ks, const T* Vt,
                                            const u32x4_t (&qr)[ItemRegs<T>::QU], int qt,
                                            const Item& it, void* __restrict__ o_, int d,
@@ -350,7 +357,7 @@ __device__ __forceinline__ void query_tile(const u32x4_t* Ks, const T* Vt,
     store_row_mx((uint8_t*)o_ + (size_t)(s0 + i) * d + (size_t)h * 64, osc, s0 + i, h * 64, d, g, v,
                  i < L);
   } else if (i < L) {
-    T* orow = (T*)o_ + (size_t)(s0 + i) * d + (size_t)h * 64;
+    OT* orow = (OT*)o_ + (size_t)(s0 + i) * d + (size_t)h * 64;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
       store_quad(orow + dt * 16 + 4 * g, oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv,
@@ -362,7 +369,7 @@ __device__ __forceinline__ void query_tile(const u32x4_t* Ks, const T* Vt,
 // registers: each wave its query tiles wave and wave + 4.  Windows of 97 to
 // 112 tokens (the common full window) skip the eighth key tile; windows of
 // more than 112 mask the eighth only; shorter ones mask every tile.
-template <typename T, bool MX>
+template <typename T, typename OT, bool MX>
 __device__ __forceinline__ void compute_item(const u32x4_t* Ks, const T* Vt,
                                              const u32x4_t (&qreg)[2][ItemRegs<T>::QU],
                                              const Item& it, void* __restrict__ o_, int d,
@@ -373,55 +380,61 @@ __device__ __forceinline__ void compute_item(const u32x4_t* Ks, const T* Vt,
     const int qt = wave + 4 * q;
     if (qt * 16 >= it.L) break;
     if (it.L > 112)
-      query_tile<T, MX, 8, false>(Ks, Vt, qreg[q], qt, it, o_, d, osc, lane);
+      query_tile<T, OT, MX, 8, false>(Ks, Vt, qreg[q], qt, it, o_, d, osc, lane);
     else if (it.L > 96)
-      query_tile<T, MX, 7, false>(Ks, Vt, qreg[q], qt, it, o_, d, osc, lane);
+      query_tile<T, OT, MX, 7, false>(Ks, Vt, qreg[q], qt, it, o_, d, osc, lane);
     else
-      query_tile<T, MX, 8, true>(Ks, Vt, qreg[q], qt, it, o_, d, osc, lane);
+      query_tile<T, OT, MX, 8, true>(Ks, Vt, qreg[q], qt, it, o_, d, osc, lane);
   }
 }
 
 // One workgroup per (window, head) item, items window-major in the plan's
 // window order (longest first, so short tail windows fill the end of the
 // grid): every load issued at once, K and V to LDS, then the matrix work.
-template <typename T, bool MX>
+template <typename T, typename OT, bool MX>
 __global__ __launch_bounds__(ATT_THREADS)
 __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 2))) void attn_kernel(
     const T* __restrict__ qkv, void* __restrict__ o_, const int* __restrict__ cu,
-    const int* __restrict__ worder, int H, int d, uint8_t* __restrict__ osc) {
+    const int* __restrict__ worder, int H, int d, uint8_t* __restrict__ osc, int n_windows, int T_rows) {
   constexpr int UR = ItemRegs<T>::UR;
   constexpr int VS = VtStride<T>::value;
   __shared__ u32x4_t Ks[LMAX * UR];
   __shared__ T Vt[64 * VS];
   const int tid = threadIdx.x;
   ItemRegs<T> r;
-  const Item it = item_of((int)blockIdx.x, cu, worder, H);
+  const Item it = item_of((int)blockIdx.x, cu, worder, H, n_windows, T_rows);
+  if (!it.ok) return;  // uniform over the workgroup, before any barrier
   load_item(r, qkv, it, d, tid);
   stage_item(r, Ks, Vt, tid);
   __syncthreads();
-  compute_item<T, MX>(Ks, Vt, r.q, it, o_, d, osc, tid);
+  compute_item<T, OT, MX>(Ks, Vt, r.q, it, o_, d, osc, tid);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const void* qkv, void* o, const int* cu, const int* worder,
                             int n_windows, int H, int d, aut_dtype dt, hipStream_t s,
-                            uint8_t* o_scales) {
+                            uint8_t* o_scales, int T, bool f32_out) {
   if (n_windows <= 0) return hipSuccess;
-  // a window's rows must fit a buffer descriptor's 32-bit byte range
-  if ((size_t)LMAX * 3 * (size_t)d * (dt == AUT_FP32 ? 4 : 2) >= ((size_t)1 << 31))
+  // a window's rows must fit a buffer descriptor's 32-bit byte range; the
+  // grid's item count must fit an int
+  if (d != 64 * H || (size_t)LMAX * 3 * (size_t)d * (dt == AUT_FP32 ? 4 : 2) >= ((size_t)1 << 31) ||
+      (long long)n_windows * H >= ((long long)1 << 31))
     return hipErrorInvalidValue;
   dim3 grid(n_windows * H);
   if (dt == AUT_FP8) {
     if (d % 128 || !o_scales) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_kernel<bf16_t, true>), grid, dim3(ATT_THREADS), 0, s,
-                       (const bf16_t*)qkv, o, cu, worder, H, d, o_scales);
+    hipLaunchKernelGGL((attn_kernel<bf16_t, bf16_t, true>), grid, dim3(ATT_THREADS), 0, s,
+                       (const bf16_t*)qkv, o, cu, worder, H, d, o_scales, n_windows, T);
+  } else if (dt == AUT_BF16 && f32_out) {
+    hipLaunchKernelGGL((attn_kernel<bf16_t, float, false>), grid, dim3(ATT_THREADS), 0, s,
+                       (const bf16_t*)qkv, o, cu, worder, H, d, (uint8_t*)nullptr, n_windows, T);
   } else if (dt == AUT_BF16) {
-    hipLaunchKernelGGL((attn_kernel<bf16_t, false>), grid, dim3(ATT_THREADS), 0, s,
-                       (const bf16_t*)qkv, o, cu, worder, H, d, (uint8_t*)nullptr);
+    hipLaunchKernelGGL((attn_kernel<bf16_t, bf16_t, false>), grid, dim3(ATT_THREADS), 0, s,
+                       (const bf16_t*)qkv, o, cu, worder, H, d, (uint8_t*)nullptr, n_windows, T);
   } else {
-    hipLaunchKernelGGL((attn_kernel<float, false>), grid, dim3(ATT_THREADS), 0, s,
-                       (const float*)qkv, o, cu, worder, H, d, (uint8_t*)nullptr);
+    hipLaunchKernelGGL((attn_kernel<float, float, false>), grid, dim3(ATT_THREADS), 0, s,
+                       (const float*)qkv, o, cu, worder, H, d, (uint8_t*)nullptr, n_windows, T);
   }
   return hipGetLastError();
 }

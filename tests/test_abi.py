@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = aut.lib()
     names = declared_functions()
-    assert len(names) == len(aut.SIGNATURES) == 31
+    assert len(names) == len(aut.SIGNATURES) == 32
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(aut.SIGNATURES), "binding and header disagree"
@@ -299,6 +299,26 @@ def test_mx_primitive_argument_checks():
     assert L.aut_mx_matmul(None, None, 4, None, None, 6, 128, None, None) == 2   # N % 4
     assert L.aut_mx_matmul(None, None, 4, None, None, 8, 96, None, None) == 1    # K % 128
     assert L.aut_mx_matmul(None, None, 4, None, None, 8, 128, None, None) == 1   # NULL
+
+
+def test_attention_argument_checks_before_launch():
+    """aut_attention refuses bad counts, dtype pairs, head counts, NULL and
+    misaligned pointers on the host, before any GPU call."""
+    L = aut.lib()
+    fp32, bf16, fp8 = (aut.DTYPES[k] for k in ("fp32", "bf16", "fp8"))
+    p = 4096  # a non-NULL, 16-byte aligned stand-in (never dereferenced: the checks fail first)
+    assert L.aut_attention(p, -1, 20, p, p, 1, bf16, bf16, p, None, None) == 1          # rows < 0
+    assert L.aut_attention(p, 10, 20, p, p, -1, bf16, bf16, p, None, None) == 1         # windows < 0
+    assert L.aut_attention(p, 10, 20, p, p, 1, fp32, bf16, p, None, None) == 2          # fp32 -> bf16
+    assert L.aut_attention(p, 10, 20, p, p, 1, fp32, fp8, p, p, None) == 2              # fp32 -> fp8
+    assert L.aut_attention(p, 10, 0, p, p, 1, bf16, bf16, p, None, None) == 2           # no head
+    assert L.aut_attention(p, 10, 3, p, p, 1, bf16, fp8, p, p, None) == 2               # odd heads, fp8
+    assert L.aut_attention(p, 10, 65, p, p, 1, bf16, bf16, p, None, None) == 2          # too many heads
+    assert L.aut_attention(None, 0, 20, None, None, 0, bf16, bf16, None, None, None) == 0  # nothing to do
+    assert L.aut_attention(None, 10, 20, p, p, 1, bf16, bf16, p, None, None) == 1       # NULL qkv
+    assert L.aut_attention(p, 10, 2, p, p, 1, bf16, fp8, p, None, None) == 1            # NULL scales
+    assert L.aut_attention(p + 8, 10, 20, p, p, 1, bf16, bf16, p, None, None) == 1      # misaligned qkv
+    assert L.aut_attention(p, 10, 20, p + 2, p, 1, bf16, bf16, p, None, None) == 1      # misaligned table
 
 
 def test_mx_scale_layout_reindex():
