@@ -436,10 +436,10 @@ aut_status aut_layernorm(const float* x, int64_t rows, int32_t d, const float* g
  *   out:          device [rows, d] of out_dtype, 16-byte aligned
  * Rows of no window are not written.  A window outside rows [0, rows), longer
  * than 128 rows or named by an order entry outside [0, n_windows) is skipped
- * (its rows are not written).  The caller owns every buffer.  Returns
- * INVALID_ARG for NULL pointers, misalignment or negative counts,
- * UNSUPPORTED for other dtype pairs or head counts.  Asynchronous on
- * `stream`. */
+ * (its rows are not written).  heads from 1 to 64, rows below 2^31.  The
+ * caller owns every buffer.  Returns INVALID_ARG for NULL pointers,
+ * misalignment or negative counts, UNSUPPORTED for other dtype pairs, head
+ * counts or row counts.  Asynchronous on `stream`. */
 aut_status aut_attention(const void* qkv, int64_t rows, int32_t heads, const int32_t* cu_seqlens,
                          const int32_t* window_order, int32_t n_windows, aut_dtype in_dtype,
                          aut_dtype out_dtype, void* out, uint8_t* out_scales, void* stream);
