@@ -578,9 +578,12 @@ WsLayout ws_layout(const aut_plan_t& p, aut_dtype dt) {
   const size_t cs = f8c ? std::max<size_t>(g.C * es, (size_t)conv_cp(g)) : g.C * es;
   const size_t per_chunk = (size_t)g.h1 * g.w1 * cs;
   const size_t max_nb = std::max<size_t>(1, ((size_t)1 << 31) / per_chunk - 1);
-  W.nb = (int)std::min<size_t>(std::min<size_t>((size_t)p.cfg.conv_chunksize, nch), max_nb);
-  if (dt != AUT_FP32) W.nb = conv_batch_chunks((int)nch, W.nb, g, f8c);
-  const size_t nb = (size_t)W.nb;
+  const size_t cap = std::min<size_t>(std::min<size_t>((size_t)p.cfg.conv_chunksize, nch), max_nb);
+  W.nb = dt != AUT_FP32 ? conv_batch_chunks((int)nch, (int)cap, g, f8c) : (int)cap;
+  // the batch buffers hold cap chunks, not the chosen W.nb <= cap: cap never
+  // shrinks as the plan grows, so a workspace sized for a plan covers every
+  // plan with fewer chunks (a stream's steps use the whole request's size)
+  const size_t nb = cap;
   W.chunks = take(nch * sizeof(aut_chunk));
   W.rowmap = take(T * 4);
   W.cu = take((nw + 1) * 4);

@@ -201,6 +201,22 @@ def test_stream_workspace_covers_each_step():
             assert aut.workspace_bytes(cfg, aut.plan(cfg, [L]), "bf16") <= n.value
 
 
+@pytest.mark.parametrize("dtype,mask", [("bf16", 0), ("fp8", 63)])
+def test_workspace_never_shrinks_as_a_request_grows(dtype, mask):
+    """A workspace sized for one request covers every shorter request (what a
+    stream's steps rely on): the full-width model at the default conv batch
+    size and at the largest, over lengths around the chunk counts where the
+    conv batches change size."""
+    cfg_d = dict(si.model_config("wide"), fp8_gemms=mask)
+    for cs in (500, 8192):
+        cfg = aut.config(dict(cfg_d, conv_chunksize=cs))
+        prev = 0
+        for L in list(range(100, 2000, 97)) + list(range(40000, 160000, 3100)):
+            n = aut.workspace_bytes(cfg, aut.plan(cfg, [L]), dtype)
+            assert n >= prev, (cs, L, n, prev)
+            prev = n
+
+
 def test_audio_rows_vs_oracle():
     """aut_audio_rows (host) against the oracle's placeholder positions."""
     rng = np.random.default_rng(17)
